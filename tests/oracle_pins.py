@@ -1,0 +1,325 @@
+"""Pins for the oracle: checks against what the pages and the mathematics fix.
+
+Each pin is a function that raises AssertionError when the oracle is wrong.
+They look up oracle functions through the module at call time, so the mutant
+tests can plant a mistake in the oracle and show that some pin catches it.
+
+The flat element offset of the pool layout, written out here independently of
+the oracle's multi-dimensional indexing, is
+
+    ((((b * NL + l) * 2 + kv) * H + h) * 16 + s) * D + d
+
+for block b, layer l, kv in {0: key, 1: value}, head h, slot s, dim d
+(LLM inference batching, faangrind, data model: [layers, 2, heads, 16, 128]
+per block).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.brute as brute
+import oracle.paged as paged
+import oracle.pool as opool
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_arithmetic.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def flat_offset(b, l, kv, h, s, d, NL, H, D):
+    return ((((b * NL + l) * 2 + kv) * H + h) * 16 + s) * D + d
+
+
+def _page_in_flat(num_blocks, NL, H, D, layer, table, K, V, fill=np.uint16(0x7E00)):
+    """Write contiguous K/V ([H, L, D] uint16) into a flat pool with explicit offsets."""
+    L = K.shape[1]
+    flat = np.full(num_blocks * NL * 2 * H * 16 * D, fill, dtype=np.uint16)
+    dd = np.arange(D)
+    for h in range(H):
+        for j in range(L):
+            b = int(table[j // 16])
+            s = j % 16
+            flat[flat_offset(b, layer, 0, h, s, 0, NL, H, D) + dd] = K[h, j]
+            flat[flat_offset(b, layer, 1, h, s, 0, NL, H, D) + dd] = V[h, j]
+    return flat.reshape(num_blocks, NL, 2, H, 16, D)
+
+
+def _rand_bits(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _f64(bits):
+    return np.asarray(bits).view(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------- pool arithmetic
+
+def pin_block_arithmetic():
+    g = golden()
+    three = g["three_requests_rounding"]
+    per = [opool.blocks_needed(n) for n in three["lengths"]]
+    assert per == three["block_size_16"]["per_request"]
+    assert sum(per) == three["block_size_16"]["blocks"]
+    assert sum(per) * 16 == three["block_size_16"]["slots"]
+    assert sum(per) * 16 - sum(three["lengths"]) == three["block_size_16"]["unused_slots"]
+    assert sum(three["lengths"]) == three["logical_tokens"]
+    per4 = [opool.blocks_needed(n, 4) for n in three["lengths"]]
+    assert sum(per4) == three["block_size_4"]["table_entries"]
+    assert sum(per4) * 4 == three["block_size_4"]["slots"]
+    p600 = g["paged_600_tokens"]
+    nb = opool.blocks_needed(p600["tokens"])
+    assert nb == p600["blocks"] and nb * 16 == p600["slots"]
+    assert nb * 16 - p600["tokens"] == p600["wasted_slots"]
+    assert nb * 16 * p600["bytes_per_token"] == p600["bytes"]
+    assert opool.blocks_needed(g["request_2300_tokens"]["tokens"]) == g["request_2300_tokens"]["blocks"]
+
+
+def pin_pool_capacity():
+    g = golden()["seven_b_pool"]
+    # every block holds [layers, 2, heads, 16, head_dim] FP16
+    block_shape = (g["layers"], 2, g["heads"], g["block_tokens"], g["head_dim"])
+    assert int(np.prod(block_shape)) * g["bytes_per_element"] == g["bytes_per_block"]
+    assert 2 * g["layers"] * g["heads"] * g["head_dim"] * g["bytes_per_element"] == g["bytes_per_token"]
+    assert g["pool_bytes"] // g["bytes_per_block"] == g["num_blocks"]
+    assert g["num_blocks"] * g["block_tokens"] == g["pool_tokens"]
+    assert round(g["average_request_tokens"] * g["bytes_per_token"] / 1e9, 2) == g["average_request_gb"]
+    assert round(g["max_request_tokens"] * g["bytes_per_token"] / 1e9, 2) == g["max_request_gb"]
+    for tokens, fit in ((g["average_request_tokens"], g["average_requests_that_fit"]),
+                        (g["max_request_tokens"], g["max_requests_that_fit"])):
+        pool = opool.BlockPool(g["num_blocks"])
+        count = 0
+        while True:
+            try:
+                pool.alloc(opool.blocks_needed(tokens))
+            except opool.OutOfBlocks:
+                break
+            count += 1
+        assert count == fit, (tokens, count, fit)
+    m = golden()["admission_margin"]
+    assert round(m["fraction"] * g["num_blocks"]) == m["blocks"]
+
+
+def pin_pool_semantics():
+    # free list 0..N-1, pop() from the end, release appends in the order given
+    p = opool.BlockPool(8)
+    assert p.alloc(3) == [7, 6, 5]
+    p.release([6, 7])
+    assert p.free == [0, 1, 2, 3, 4, 6, 7]
+    assert p.alloc(1) == [7]
+    # all or nothing
+    before = list(p.free)
+    try:
+        p.alloc(len(before) + 1)
+        raise AssertionError("over-allocation accepted")
+    except opool.OutOfBlocks:
+        pass
+    assert p.free == before
+    # shared blocks return only at count zero; over-release is refused with no change
+    p.share([5])
+    assert p.ref[5] == 2
+    p.release([5])
+    assert p.ref[5] == 1 and 5 not in p.free
+    try:
+        p.release([5, 5])
+        raise AssertionError("double free accepted")
+    except opool.DoubleFree:
+        pass
+    assert p.ref[5] == 1
+    p.release([5])
+    assert p.free[-1] == 5 and p.ref[5] == 0
+    # grow: P5-style all-or-nothing growth of a table
+    t = []
+    assert p.grow(t, 33) and len(t) == 3
+    assert not p.grow(t, 16 * 100) and len(t) == 3
+
+
+# ---------------------------------------------------------------- layout / append / gather
+
+def pin_append_offsets(seed=11):
+    rng = np.random.default_rng(seed)
+    NB, NL, H, D = 9, 3, 2, 8
+    pool = _rand_bits(rng, (NB, NL, 2, H, 16, D))
+    table = np.array([[4, 1, 7], [0, 8, 2]], dtype=np.int32)
+    positions = np.array([0, 15, 16, 33, 17, 47], dtype=np.int32)
+    rows = np.array([0, 0, 0, 0, 1, 1], dtype=np.int32)
+    k = _rand_bits(rng, (6, H, D))
+    v = _rand_bits(rng, (6, H, D))
+    layer = 2
+    got = paged.append(pool, layer, k, v, positions, rows, table).reshape(-1)
+    want = pool.reshape(-1).copy()
+    for t in range(6):
+        b = int(table[rows[t], positions[t] // 16])
+        s = int(positions[t] % 16)
+        for h in range(H):
+            for d in range(D):
+                want[flat_offset(b, layer, 0, h, s, d, NL, H, D)] = k[t, h, d]
+                want[flat_offset(b, layer, 1, h, s, d, NL, H, D)] = v[t, h, d]
+    assert np.array_equal(got, want)
+
+
+def pin_gather_roundtrip(seed=12):
+    rng = np.random.default_rng(seed)
+    NB, NL, H, D = 12, 2, 3, 8
+    for L in (1, 5, 16, 17, 40):
+        table = rng.permutation(NB)[: -(-L // 16)].astype(np.int32)
+        K = _rand_bits(rng, (H, L, D))
+        V = _rand_bits(rng, (H, L, D))
+        pool = _page_in_flat(NB, NL, H, D, 1, table, K, V)
+        gk, gv = paged.gather_kv(pool[:, 1], table, L)
+        assert gk.shape == (H, L, D)
+        assert np.array_equal(gk, _f64(K)) and np.array_equal(gv, _f64(V))
+
+
+# ---------------------------------------------------------------- attention
+
+def pin_bruteforce(seed=13):
+    rng = np.random.default_rng(seed)
+    for H, D, lens, qn in ((1, 4, [1, 3, 17], [1, 2, 5]), (2, 8, [16, 33], [1, 8]), (32, 128, [20], [3])):
+        NB = sum(-(-L // 16) for L in lens) + 2
+        NL = 1
+        ids = rng.permutation(NB)
+        pos = 0
+        tables = np.zeros((len(lens), 4), dtype=np.int32)
+        conts = []
+        pool = np.full((NB, NL, 2, H, 16, D), np.uint16(0x7E00), dtype=np.uint16)
+        for r, L in enumerate(lens):
+            nb = -(-L // 16)
+            tables[r, :nb] = ids[pos:pos + nb]
+            pos += nb
+            K = _rand_bits(rng, (H, L, D))
+            V = _rand_bits(rng, (H, L, D))
+            sub = _page_in_flat(NB, NL, H, D, 0, tables[r], K, V, fill=np.uint16(0))
+            used = np.zeros(NB, dtype=bool)
+            used[tables[r, :nb]] = True
+            pool[used] = sub[used]
+            conts.append((K, V))
+        qs = np.concatenate([[0], np.cumsum(qn)])
+        q = _rand_bits(rng, (int(qs[-1]), H, D))
+        scale = 1.0 / math.sqrt(D)
+        out = paged.chunked_prefill(pool[:, 0], q, qs, tables, lens, scale)
+        for r, L in enumerate(lens):
+            K, V = (_f64(x) for x in conts[r])
+            n = qn[r]
+            for i in range(n):
+                p = L - n + i
+                for h in range(H):
+                    want = brute.attend_one(list(_f64(q[qs[r] + i, h])), [list(K[h, j]) for j in range(p + 1)],
+                                            [list(V[h, j]) for j in range(p + 1)], scale)
+                    np.testing.assert_allclose(out[qs[r] + i, h], want, rtol=0, atol=1e-12)
+
+
+def pin_closed_forms(seed=14):
+    rng = np.random.default_rng(seed)
+    H, D = 2, 8
+    # hand-worked: q = e0, keys e0 and e1, values (1,2..) and (3,4..), scale 1 -> (e*v0 + v1) / (e + 1)
+    q = np.zeros((1, 1, 2))
+    q[0, 0, 0] = 1.0
+    K = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    V = np.array([[[1.0, 2.0], [3.0, 4.0]]])
+    out = paged.attention(q, K, V, [1], 1.0)[0, 0]
+    e = math.e
+    np.testing.assert_allclose(out, [(e * 1 + 3) / (e + 1), (e * 2 + 4) / (e + 1)], rtol=1e-15)
+    # the same query at position 0 sees only key 0 -> v0
+    np.testing.assert_array_equal(paged.attention(q, K, V, [0], 1.0)[0, 0], V[0, 0])
+    # a scale of 2 doubles the score gap
+    out2 = paged.attention(q, K, V, [1], 2.0)[0, 0]
+    np.testing.assert_allclose(out2, [(e ** 2 * 1 + 3) / (e ** 2 + 1), (e ** 2 * 2 + 4) / (e ** 2 + 1)], rtol=1e-15)
+    # context of length 1 returns V exactly
+    K1 = _f64(_rand_bits(rng, (H, 1, D)))
+    V1 = _f64(_rand_bits(rng, (H, 1, D)))
+    q1 = _f64(_rand_bits(rng, (1, H, D)))
+    np.testing.assert_array_equal(paged.attention(q1, K1, V1, [0], 0.3)[0], V1[:, 0])
+    # q = 0: uniform weights -> mean of the values
+    L = 13
+    Kr = _f64(_rand_bits(rng, (H, L, D)))
+    Vr = _f64(_rand_bits(rng, (H, L, D)))
+    np.testing.assert_allclose(paged.attention(np.zeros((1, H, D)), Kr, Vr, [L - 1], 0.3)[0], Vr.mean(axis=1),
+                               rtol=0, atol=1e-14)
+    # row-constant V returns the constant
+    Vc = np.full((H, L, D), 0.625)
+    np.testing.assert_allclose(paged.attention(q1, Kr, Vc, [L - 1], 0.3)[0], 0.625, rtol=0, atol=1e-15)
+    # one key dominating by a gap g returns its value within (L-1) e^-g max|V|
+    Kd = np.zeros((1, L, 2))
+    Kd[0, 5, 0] = 30.0
+    qd = np.array([[[1.0, 0.0]]])
+    Vd = _f64(_rand_bits(rng, (1, L, 2)))
+    got = paged.attention(qd, Kd, Vd, [L - 1], 1.0)[0, 0]
+    assert np.max(np.abs(got - Vd[0, 5])) <= (L - 1) * math.exp(-30.0) * np.max(np.abs(Vd)) * 2
+
+
+def pin_decode_reads_own_token(seed=15):
+    g = golden()["decode_reads_own_token"]
+    rng = np.random.default_rng(seed)
+    H, D = 1, 8
+    L = g["cache_after_step_1"]
+    table = np.arange(-(-L // 16), dtype=np.int32)
+    K = np.zeros((H, L, D), dtype=np.float16)
+    V = np.zeros((H, L, D), dtype=np.float16)
+    V[0, L - 1] = 1.0          # only the newest position carries value
+    K[0, L - 1, 0] = 8.0       # and it wins the softmax by a wide margin
+    pool = _page_in_flat(len(table), 1, H, D, 0, table, K.view(np.uint16), V.view(np.uint16), fill=np.uint16(0))
+    q = np.zeros((1, H, D), dtype=np.float16)
+    q[0, 0, 0] = 8.0
+    out = paged.decode(pool[:, 0], q.view(np.uint16), table[None, :], [L], 1.0)
+    gk, _ = paged.gather_kv(pool[:, 0], table, L)
+    assert gk.shape[1] == g["positions_read_in_step_1"]
+    assert out[0, 0, 0] > 0.99
+    assert g["prompt_tokens"] + g["answer_tokens"] - 1 == g["final_cache"]
+
+
+def pin_invariants(seed=16):
+    rng = np.random.default_rng(seed)
+    H, D, NB = 2, 16, 24
+    lens = [37, 16, 5]
+    nbs = [-(-L // 16) for L in lens]
+    pool = _rand_bits(rng, (NB, 1, 2, H, 16, D))
+    tables = np.zeros((3, 3), dtype=np.int32)
+    ids = rng.permutation(NB)
+    pos = 0
+    for r, nb in enumerate(nbs):
+        tables[r, :nb] = ids[pos:pos + nb]
+        pos += nb
+    q = _rand_bits(rng, (3, H, D))
+    base = paged.decode(pool[:, 0], q, tables, lens, 0.25)
+    # permuting physical ids (moving block contents with them) changes nothing, bit for bit
+    perm = rng.permutation(NB)
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    tables2 = perm[tables].astype(np.int32)
+    np.testing.assert_array_equal(paged.decode(pool2[:, 0], q, tables2, lens, 0.25), base)
+    # a prefix shared through the same ids equals private copies of it
+    shared = tables.copy()
+    shared[1, 0] = tables[0, 0]
+    priv_pool = pool.copy()
+    priv_pool[tables[1, 0]] = pool[tables[0, 0]]
+    np.testing.assert_array_equal(paged.decode(pool[:, 0], q, shared, lens, 0.25),
+                                  paged.decode(priv_pool[:, 0], q, tables, lens, 0.25))
+    # adding one vector u to every key shifts every score equally
+    K, V = paged.gather_kv(pool[:, 0], tables[0], lens[0])
+    u = rng.standard_normal((H, 1, D))
+    qf = _f64(q[0:1])
+    a = paged.attention(qf, K, V, [lens[0] - 1], 0.25)
+    b = paged.attention(qf, K + u, V, [lens[0] - 1], 0.25)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # a chunk of one query is a decode; chunk query i equals a decode over its prefix
+    qs = np.array([0, 4, 5, 6])
+    qc = _rand_bits(rng, (6, H, D))
+    pre = paged.chunked_prefill(pool[:, 0], qc, qs, tables, lens, 0.25)
+    for i in range(4):
+        p = lens[0] - 4 + i
+        one = paged.decode(pool[:, 0], qc[i:i + 1], tables[0:1], [p + 1], 0.25)
+        # equal up to the summation order of the library matmul
+        np.testing.assert_allclose(pre[i], one[0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(pre[4], paged.decode(pool[:, 0], qc[4:5], tables[1:2], [lens[1]], 0.25)[0],
+                               rtol=0, atol=1e-14)
+
+
+ALL_PINS = [pin_block_arithmetic, pin_pool_capacity, pin_pool_semantics, pin_append_offsets,
+            pin_gather_roundtrip, pin_bruteforce, pin_closed_forms, pin_decode_reads_own_token, pin_invariants]

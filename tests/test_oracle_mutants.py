@@ -1,0 +1,92 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least
+one pin fails for each.  This shows the pins constrain every part of the
+oracle rather than restating it."""
+import numpy as np
+import pytest
+
+import oracle.paged as paged
+import oracle.pool as opool
+from tests import oracle_pins
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+_attention = paged.attention
+_gather = paged.gather_kv
+_locate = paged.locate
+
+
+def _attn_no_scale(q, K, V, pos, scale):
+    return _attention(q, K, V, pos, 1.0)
+
+
+def _attn_swap_kv(q, K, V, pos, scale):
+    return _attention(q, V, K, pos, scale)
+
+
+def _attn_hide_own(q, K, V, pos, scale):
+    pos = np.asarray(pos)
+    if np.all(pos >= 1):
+        return _attention(q, K, V, pos - 1, scale)
+    return _attention(q, K, V, pos, scale)
+
+
+def _attn_neg_sign(q, K, V, pos, scale):
+    return _attention(q, K, V, pos, -scale)
+
+
+def _gather_reverse_slots(pool_layer, row, L, block_size=16):
+    K, V = _gather(pool_layer, row, L, block_size)
+    if L >= 2:
+        K = K.copy(); V = V.copy()
+        K[:, :2] = K[:, 1::-1]
+        V[:, :2] = V[:, 1::-1]
+    return K, V
+
+
+def _gather_drop_tail(pool_layer, row, L, block_size=16):
+    full = (L // block_size) * block_size
+    if full and full != L:
+        K, V = _gather(pool_layer, row, full, block_size)
+        K2, V2 = _gather(pool_layer, row, L, block_size)
+        K2 = K2.copy(); V2 = V2.copy()
+        K2[:, full:] = K[:, -1:]
+        V2[:, full:] = V[:, -1:]
+        return K2, V2
+    return _gather(pool_layer, row, L, block_size)
+
+
+def _locate_swapped(row, position, block_size=16):
+    return int(row[position % block_size if position % block_size < len(row) else 0]), position // block_size % block_size
+
+
+def _blocks_floor(n, block_size=16):
+    return int(n) // block_size
+
+
+MUTANTS = [
+    ("attention", _attn_no_scale),
+    ("attention", _attn_swap_kv),
+    ("attention", _attn_hide_own),
+    ("attention", _attn_neg_sign),
+    ("gather_kv", _gather_reverse_slots),
+    ("gather_kv", _gather_drop_tail),
+    ("locate", _locate_swapped),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTANTS, ids=[f"{n}:{f.__name__}" for n, f in MUTANTS])
+def test_mutant_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(paged, name, fn)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {fn.__name__}"
+
+
+def test_pool_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(opool, "blocks_needed", _blocks_floor)
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_block_arithmetic()
