@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of the average-mix batch over all 32 layers.
+
+A step is the whole hot path for one batch of 32 decode rows:
+  host  grow block tables through the C++ block pool where a row crosses a
+        16-token boundary, upload tables / lengths / positions (pinned, async);
+  GPU   for each of 32 layers: KV append of the 32 new tokens, then paged
+        decode attention (split-K kernel + merge kernel).
+Rows advance one token per step, as in a real decode loop.
+
+Workload: 32 rows, context = lognormal prompt (mean 1,250, clipped to
+[50, 8000]) + U{1..300} generated tokens; KV pool of 7,152 blocks x
+[32 layers, 2, 32 heads, 16, 128] FP16 (60 GB), blocks handed out from a
+shuffled free list, values N(0,1).  Inputs are resident in HBM before the
+timed region starts.
+
+Prints one JSON line.  `value` is KV-tokens/s where one KV-token is a cached
+token read across all 32 layers (524,288 bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV-tokens/s + HBM TB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+LAYER_TOKEN_BYTES = 2 * 32 * 128 * 2          # K+V of one token, one layer
+STEP_TOKEN_BYTES = LAYER_TOKEN_BYTES * 32       # all 32 layers
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(each GPU would serve its own requests or its own heads with no exchange inside attention)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_pkv_amd as pkv
+    from workloads import SCALE, c2_average_mix, fill_normal_fp16_device
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    NB, NL, H, D = 7152, 32, 32, 128
+    batch = c2_average_mix(seed=args.seed, with_pool=False)
+    R = batch.rows
+    stride = batch.bt_stride
+    total_steps = args.warmup + args.steps
+    lens0 = batch.context_lens.astype(np.int64)
+    max_ctx = int(lens0.max()) + total_steps
+    if -(-max_ctx // 16) > stride:
+        raise SystemExit("table stride too small for the run length")
+
+    log(args, f"allocating pool {NB}x{NL}x2x{H}x16x{D} FP16 ({NB * NL * 2 * H * 16 * D * 2 / 1e9:.1f} GB)")
+    pool_d = torch.empty((NB, NL, 2, H, 16, D), dtype=torch.int16, device=dev)
+    fill_normal_fp16_device(pool_d, seed=1000 + args.seed)
+    cache = pkv.PagedCache(pool_d)
+
+    # host block pool: shuffled free list, rows allocated in order
+    bp = pkv.BlockPool(NB, batch.free_list)
+    tables = np.zeros((R, stride), dtype=np.int32)
+    tlen = np.zeros(R, dtype=np.int64)
+    for r in range(R):
+        tlen[r] = bp.grow(tables[r], 0, int(lens0[r]))
+    for r in range(R):  # the C++ pool hands out the ids the generator's LIFO reading predicts
+        assert np.array_equal(tables[r, :tlen[r]], batch.block_tables[r, :tlen[r]])
+
+    q_d = torch.from_numpy(batch.q.view(np.int16)).to(dev)         # [NL, R, H, D]
+    k_d = torch.from_numpy(batch.k_new.view(np.int16)).to(dev)
+    v_d = torch.from_numpy(batch.v_new.view(np.int16)).to(dev)
+    out_d = torch.empty((NL, R, H, D), dtype=torch.float16, device=dev)
+    rot_d = torch.arange(R, dtype=torch.int32, device=dev)
+    tables_d = torch.empty((R, stride), dtype=torch.int32, device=dev)
+    lens_d = torch.empty(R, dtype=torch.int32, device=dev)
+    pos_d = torch.empty(R, dtype=torch.int32, device=dev)
+    ws_bytes = pkv.decode_workspace_size(cache, R, max_ctx)
+    ws_d = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    # pinned staging, one set per step so the host never overwrites a buffer in flight
+    stage = [torch.empty(R * stride + 2 * R, dtype=torch.int32, pin_memory=True) for _ in range(total_steps)]
+
+    # ---------------- CPU baseline input: blocks read back before any kernel touches the pool
+    cpu_sample = None
+    if not args.no_cpu_baseline:
+        ids = np.unique(np.concatenate([tables[r, :tlen[r]] for r in range(R)]))
+        slab = pool_d[torch.from_numpy(ids.astype(np.int64)).to(dev), 0].cpu().numpy().view(np.uint16)
+        cpu_sample = (ids, slab)
+
+    def host_step(k):
+        """Grow tables for this step's new token, stage the upload."""
+        lens = lens0 + k
+        for r in range(R):
+            if tlen[r] * 16 < lens[r]:
+                tlen[r] = bp.grow(tables[r], int(tlen[r]), int(lens[r]))
+        buf = stage[k]
+        a = buf.numpy()
+        a[: R * stride] = tables.reshape(-1)
+        a[R * stride: R * stride + R] = lens
+        a[R * stride + R:] = lens - 1
+        tables_d.copy_(buf[: R * stride].view(R, stride), non_blocking=True)
+        lens_d.copy_(buf[R * stride: R * stride + R], non_blocking=True)
+        pos_d.copy_(buf[R * stride + R:], non_blocking=True)
+        return int(lens.sum())
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    # one (start, end) event pair per timed (step, layer) launch
+    ev_app = [(events(NL), events(NL)) for _ in range(args.steps)]
+    ev_dec = [(events(NL), events(NL)) for _ in range(args.steps)]
+
+    def gpu_step(i):
+        for l in range(NL):
+            if i is not None:
+                ev_app[i][0][l].record(stream)
+            pkv.append(cache, l, k_d[l], v_d[l], pos_d, rot_d, tables_d, stream=stream)
+            if i is not None:
+                ev_app[i][1][l].record(stream)
+                ev_dec[i][0][l].record(stream)
+            pkv.decode_attention(cache, l, out_d[l], q_d[l], tables_d, lens_d, max_ctx, SCALE, ws_d, stream=stream)
+            if i is not None:
+                ev_dec[i][1][l].record(stream)
+
+    log(args, f"rows={R} sum_context={int(lens0.sum())} max_context={int(lens0.max())} ws={ws_bytes}")
+    parity = None
+    step0_out = None
+    for k in range(args.warmup):
+        host_step(k)
+        gpu_step(None)
+        if k == 0:
+            torch.cuda.synchronize()
+            step0_out = out_d[0].cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    tokens = 0
+    dec_bytes = 0
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    for i, k in enumerate(range(args.warmup, total_steps)):
+        step_tokens = host_step(k)
+        tokens += step_tokens
+        dec_bytes += step_tokens * LAYER_TOKEN_BYTES * NL
+        gpu_step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = t_start.elapsed_time(t_end)
+    log(args, f"timed {args.steps} steps: {elapsed_ms:.2f} ms (wall {wall * 1e3:.1f} ms)")
+
+    dec_all = [ev_dec[i][0][l].elapsed_time(ev_dec[i][1][l]) for i in range(args.steps) for l in range(NL)]
+    app_all = [ev_app[i][0][l].elapsed_time(ev_app[i][1][l]) for i in range(args.steps) for l in range(NL)]
+    dec_avg_ms = float(np.mean(dec_all))
+    bytes_per_decode = dec_bytes / (args.steps * NL)
+    achieved = bytes_per_decode / (dec_avg_ms / 1e3) / 1e9
+    app_avg_us = float(np.mean(app_all)) * 1e3
+
+    ms_per_step = elapsed_ms / args.steps
+    value = tokens / (elapsed_ms / 1e3)
+
+    # ---------------- CPU baseline leg: the oracle as it stands, timed on a bounded sample
+    # (layer 0 of step 0, rows in turn).  The oracle appends the step-0 tokens
+    # itself; its outputs are also compared with the GPU's step-0 outputs.
+    parity = None
+    cpu_baseline = None
+    if cpu_sample is not None:
+        import threadpoolctl
+
+        import oracle.paged as opaged
+
+        ids, slab = cpu_sample
+        index = {int(bk): i for i, bk in enumerate(ids)}
+
+        class Blocks:
+            def __getitem__(self, bk):
+                return slab[index[int(bk)]]
+
+        tbl0 = batch.block_tables
+        pos0 = (lens0 - 1).astype(np.int64)
+        for r in range(R):
+            bk, s = opaged.locate(tbl0[r], int(pos0[r]))
+            slab[index[bk], 0, :, s, :] = batch.k_new[0, r]
+            slab[index[bk], 1, :, s, :] = batch.v_new[0, r]
+        t0 = time.perf_counter()
+        rows_done = tok_done = bad = 0
+        max_abs = 0.0
+        while time.perf_counter() - t0 < args.cpu_seconds and rows_done < 4 * R:
+            r = rows_done % R
+            ref = opaged.decode(Blocks(), batch.q[0], tbl0, lens0, SCALE, rows=[r])[0]
+            rows_done += 1
+            tok_done += int(lens0[r])
+            if rows_done <= R:
+                err = np.abs(step0_out[r] - ref)
+                max_abs = max(max_abs, float(err.max()))
+                bad += int((err > np.maximum(2e-3, 1e-2 * np.abs(ref))).sum())
+        cpu_s = time.perf_counter() - t0
+        parity = {"layer": 0, "rows": min(rows_done, R), "max_abs": max_abs, "bad": bad, "pass": bad == 0}
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        cpu_baseline = {"value": (tok_done / NL) / cpu_s, "unit": "KV-tokens/s", "cores": int(threads),
+                        "kind": "oracle",
+                        "sample": f"fp64 oracle decode of {rows_done} (row, layer-0) tasks of the same step, "
+                                  f"{tok_done} one-layer tokens in {cpu_s:.1f} s; value = layer-tokens / 32 / s"}
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "average-mix decode step: 32 rows x 32 layers, 32 heads x 128, FP16 KV in 7152 blocks of 16",
+            "rows": R, "layers": NL, "heads": H, "head_dim": D, "num_blocks": NB,
+            "sum_context_tokens_first_step": int((lens0 + args.warmup).sum()), "seed": args.seed,
+        },
+        "hbm_tb_s": value * STEP_TOKEN_BYTES / 1e12,
+        "hbm_frac_of_peak": value * STEP_TOKEN_BYTES / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "pkv_decode_attention (split + merge launches), one layer",
+                     "avg_launch_ms": dec_avg_ms, "bytes_per_launch": bytes_per_decode,
+                     "launches": len(dec_all)},
+        "append_avg_us": app_avg_us,
+        "wall_s_timed": wall,
+        "parity_step0_layer0": parity,
+        "cpu_baseline": cpu_baseline,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * pkv.h - paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * A continuous-batching server keeps every request's attention keys and values
+ * in fixed 16-token blocks of one shared FP16 pool; a per-request block table
+ * maps logical block numbers to physical ones, a free list hands blocks out as
+ * sequences grow, and reference counts let requests share prefix blocks
+ * (LLM inference batching, faangrind.vercel.app: data model "KV pool",
+ * "block_table", "ref_count", "free_list"; Build a continuous batching server,
+ * scalablesystem.dev: "The KV Cache Block Manager (PagedAttention)" and
+ * "PagedAttention Block Table Lookup").  Each decode step appends one token's
+ * keys and values per row and attends over the row's blocks in place; a
+ * prefill chunk attends causally over its paged prefix in the same step
+ * (faangrind: "Prefill and decode share each step").
+ *
+ * This header is the whole boundary.  It uses plain C types only.
+ *
+ * Conventions for every call
+ *  - Return value: PKV_OK (0) or a negative PKV_ERR_* code.  On error nothing
+ *    has been launched or changed, and pkv_last_error() (thread-local) holds a
+ *    message.  Scalar arguments are validated on the host before any launch.
+ *  - Device pointers are owned by the caller and must stay valid until the
+ *    work queued on `stream` has finished.  The library never allocates or
+ *    frees device memory and never synchronizes the stream.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *  - Contents of device arrays (block ids, lengths, positions) are the
+ *    caller's contract: they are not copied to the host.  Kernels bounds-check
+ *    every block id against num_blocks and every table index against
+ *    bt_stride, so a bad entry yields unspecified values for that row (or an
+ *    append that is skipped) but never an out-of-bounds memory access.
+ *  - The block pool object is single-owner and not thread-safe: one scheduler
+ *    thread owns it (faangrind: "One scheduler thread owns the GPU").
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* null pointer, negative count, index out of range */
+  PKV_ERR_UNSUPPORTED = -2,   /* shape the kernels are not built for */
+  PKV_ERR_OUT_OF_BLOCKS = -3, /* allocation larger than the free list; nothing allocated */
+  PKV_ERR_DOUBLE_FREE = -4,   /* release or share of a block whose count is already 0 */
+  PKV_ERR_BAD_BLOCK = -5,     /* block id outside [0, num_blocks) */
+  PKV_ERR_WORKSPACE = -6,     /* workspace missing or smaller than the size query says */
+  PKV_ERR_HIP = -7            /* the HIP runtime refused a launch; message kept */
+};
+
+/* Message for the last error on this thread ("" when the last call succeeded). */
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * Host block pool: free list + reference counts.
+ *
+ * The free list is a stack: allocation pops ids from its top and release
+ * pushes them back in the order given (scalablesystem.dev BlockManager;
+ * Serving LLMs, sreshtalluri.github.io: "Paged KV memory" BlockPool).
+ * A block's count is 1 after allocation, +1 per share, -1 per release; it
+ * returns to the free list only at 0 (faangrind data model: "ref_count ...
+ * above 1 when n samples share one prompt"; failure list: a block freed
+ * while still referenced leaks one user's text into another's answer).
+ * Every call validates all of its ids before changing anything.
+ * ---------------------------------------------------------------------- */
+typedef struct pkv_pool pkv_pool;
+
+/* Pool of num_blocks ids with free list 0..num_blocks-1; the first
+ * allocation takes num_blocks-1.  *out receives a new pool owned by the
+ * caller (release with pkv_pool_destroy). */
+int pkv_pool_create(int32_t num_blocks, pkv_pool** out);
+
+/* Pool of num_blocks ids whose free list is free_ids[0..n_free) with
+ * free_ids[n_free-1] on top (allocated first), e.g. a shuffled list.  Ids must
+ * be distinct and in range; ids not listed start allocated with count 1. */
+int pkv_pool_create_from_list(int32_t num_blocks, const int32_t* free_ids, int32_t n_free, pkv_pool** out);
+
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Pop n ids into out_ids[0..n) (out_ids[0] = old top), each with count 1.
+ * All or nothing: with fewer than n free, returns PKV_ERR_OUT_OF_BLOCKS and
+ * changes nothing (Serving LLMs, BlockPool.grow: "False means: preempt
+ * someone"). */
+int pkv_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids);
+
+/* Count +1 for each listed id (a new sharer of a prefix block).  Every id must
+ * be allocated; otherwise PKV_ERR_DOUBLE_FREE / PKV_ERR_BAD_BLOCK and no
+ * change. */
+int pkv_ref(pkv_pool* pool, const int32_t* ids, int32_t n);
+
+/* Count -1 for each listed id; an id reaching 0 is pushed on the free list, in
+ * list order.  An id listed more times than its count is PKV_ERR_DOUBLE_FREE
+ * and nothing changes. */
+int pkv_free(pkv_pool* pool, const int32_t* ids, int32_t n);
+
+/* Grow a block table so it covers num_tokens tokens: appends
+ * ceil(num_tokens/16) - *table_len newly allocated ids to table[*table_len..]
+ * and updates *table_len.  All or nothing (PKV_ERR_OUT_OF_BLOCKS); a table
+ * that already covers num_tokens is left as is.  capacity bounds table. */
+int pkv_grow(pkv_pool* pool, int32_t* table, int32_t* table_len, int32_t capacity, int32_t num_tokens);
+
+int32_t pkv_num_free(const pkv_pool* pool);
+int32_t pkv_num_blocks(const pkv_pool* pool);
+/* Count of block id, or -1 if id is out of range. */
+int32_t pkv_ref_count(const pkv_pool* pool, int32_t id);
+/* Copies up to cap ids of the free list, bottom first, into out; returns the
+ * free-list length. */
+int32_t pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap);
+/* ceil(num_tokens / 16) (scalablesystem.dev BlockManager.blocks_needed). */
+int32_t pkv_blocks_needed(int32_t num_tokens);
+
+/* ------------------------------------------------------------------------
+ * Device KV pool descriptor.
+ *
+ * base points to caller-owned FP16 device memory laid out as
+ *   [num_blocks][num_layers][2][num_heads][block_size][head_dim]
+ * (faangrind data model: one block holds [32 layers, 2, 32 heads, 16 tokens,
+ * 128] FP16; index 0 of the "2" axis is keys, 1 is values).
+ * Supported: block_size == 16, head_dim == 128, 1 <= num_heads <= 128,
+ * num_layers >= 1, num_blocks >= 1.  Offsets are 64-bit: a 7,152-block,
+ * 32-layer pool is 60 GB.
+ * ---------------------------------------------------------------------- */
+typedef struct pkv_cache {
+  void* base;
+  int32_t num_blocks;
+  int32_t num_layers;
+  int32_t num_heads;
+  int32_t block_size;
+  int32_t head_dim;
+} pkv_cache;
+
+/* ------------------------------------------------------------------------
+ * KV append.
+ *
+ * For each new token t < num_tokens of one step (the step's flat token list
+ * tagged by request, faangrind "One step with B decode rows and a prefill
+ * chunk"): row r = request_of_token[t], position p = positions[t],
+ * block b = block_tables[r * bt_stride + p / 16], slot s = p % 16; copies the
+ * bits of k_new[t] into pool[b][layer][0][:][s][:] and of v_new[t] into
+ * pool[b][layer][1][:][s][:].  A row takes a new block every 16 tokens
+ * (faangrind scheduler step 7), so the caller grows the table first.
+ *   k_new, v_new  device FP16 [num_tokens][num_heads][128]
+ *   positions, request_of_token  device int32 [num_tokens]
+ *   block_tables  device int32 [num_rows][bt_stride]
+ * Targets must be distinct and must not be shared blocks (count 1): shared
+ * prefix blocks are immutable and a writer copies first (The inference
+ * engine, wpnews.pro: copy-on-write when a branch diverges).  A token whose
+ * row, position or block id is out of range is skipped.  num_tokens == 0 is a
+ * no-op.  Bit-exact.
+ * ---------------------------------------------------------------------- */
+int pkv_append(const pkv_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+               const int32_t* positions, const int32_t* request_of_token, int32_t num_tokens,
+               const int32_t* block_tables, int32_t num_rows, int32_t bt_stride, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention.
+ *
+ * Row r has one query q[r] (device FP16 [num_rows][num_heads][128]) at
+ * position context_lens[r]-1, and attends over its context_lens[r] cached
+ * tokens including the token appended this step (Inference Infrastructure,
+ * seeitflow.com: "Three iterations with the state written out").  For every
+ * head: out = softmax_j((q . k_j) * scale) v_j over j < context_lens[r], read
+ * through the block table in place (scalablesystem.dev "PagedAttention Block
+ * Table Lookup": no contiguous copy).  Softmax statistics are kept per tile
+ * so that tiles combine exactly (The inference engine, wpnews.pro: "IO-aware
+ * attention and quantization attack different costs").  FP16 inputs, fp32
+ * arithmetic, FP16 output rounded to nearest even:
+ *   out  device FP16 [num_rows][num_heads][128]
+ * Long contexts are split into fixed ranges of pkv_split_tokens() tokens whose
+ * partial results a second pass merges; the split depends only on the row's
+ * own length, so a row's output does not depend on its batch neighbours.
+ *   context_lens       device int32 [num_rows], each in [1, max_context_len]
+ *   max_context_len    host bound on context_lens, <= bt_stride * 16
+ *   workspace          device memory of at least
+ *                      pkv_decode_workspace_size(cache, num_rows, max_context_len)
+ *                      bytes, 256-byte aligned; contents need no
+ *                      initialisation and are scratch after the call.
+ * A context_len outside [1, max_context_len] is clamped for memory safety and
+ * gives unspecified output for that row.
+ * ---------------------------------------------------------------------- */
+size_t pkv_decode_workspace_size(const pkv_cache* cache, int32_t num_rows, int32_t max_context_len);
+int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void* out, const void* q,
+                         const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                         int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Tokens per split-K range of the decode kernel. */
+int32_t pkv_split_tokens(void);
+
+/* ------------------------------------------------------------------------
+ * Chunked-prefill attention mixed with decode rows in one launch.
+ *
+ * Row r owns queries q[query_start[r] .. query_start[r+1]) (device FP16
+ * [total_q][num_heads][128]); they are the last n_r = query_start[r+1] -
+ * query_start[r] positions of its context, L_r - n_r .. L_r - 1 with
+ * L_r = context_lens[r], and their keys and values were appended before the
+ * call.  Query i of the row sits at p = L_r - n_r + i and attends causally to
+ * keys 0..p (The inference engine, wpnews.pro: prefill "respects the causal
+ * mask").  Rows with n_r == 1 are decode rows; a prefill chunk and decode rows
+ * share the step as a flat list of request-tagged tokens (faangrind "Prefill
+ * and decode share each step").  The chunk's QK^T and PV products run on
+ * MFMA matrix cores in FP16 with fp32 accumulation.
+ *   out            device FP16 [total_q][num_heads][128]
+ *   query_start    device int32 [num_rows + 1], query_start[0] = 0,
+ *                  query_start[num_rows] = total_q
+ *   context_lens   device int32 [num_rows], n_r <= L_r <= max_context_len
+ *   max_q_per_row  host bound on n_r
+ *   workspace      >= pkv_prefill_workspace_size(...) bytes, 256-byte aligned
+ * Rows violating the bounds give unspecified output but no out-of-bounds
+ * access.
+ * ---------------------------------------------------------------------- */
+size_t pkv_prefill_workspace_size(const pkv_cache* cache, int32_t num_rows, int32_t total_q,
+                                  int32_t max_q_per_row, int32_t max_context_len);
+int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t layer, void* out, const void* q,
+                                  const int32_t* query_start, const int32_t* block_tables, int32_t bt_stride,
+                                  const int32_t* context_lens, int32_t num_rows, int32_t total_q,
+                                  int32_t max_q_per_row, int32_t max_context_len, float scale,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,199 @@
+"""Paged KV-cache attention for MI355X: Python binding of libpkv.so.
+
+Argument marshalling only.  Every step of the path runs in the library: the
+host block pool in C++, append / decode / chunked prefill in gfx950 HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  If the
+library is missing, calls raise; nothing falls back to another
+implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+
+BLOCK_SIZE = 16
+HEAD_DIM = 128
+
+PKV_OK = 0
+ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OUT_OF_BLOCKS", -4: "DOUBLE_FREE", -5: "BAD_BLOCK",
+          -6: "WORKSPACE", -7: "HIP"}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(rc: int):
+    if rc != PKV_OK:
+        raise PkvError(rc, lib().pkv_last_error().decode())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(_lib.c_i32_p)
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+def blocks_needed(num_tokens: int) -> int:
+    return int(lib().pkv_blocks_needed(int(num_tokens)))
+
+
+def split_tokens() -> int:
+    return int(lib().pkv_split_tokens())
+
+
+class BlockPool:
+    """Host block pool (free list + reference counts) owned by libpkv."""
+
+    def __init__(self, num_blocks: int, free_list=None):
+        self._h = ctypes.c_void_p()
+        if free_list is None:
+            _check(lib().pkv_pool_create(int(num_blocks), ctypes.byref(self._h)))
+        else:
+            fl = _i32(free_list)
+            _check(lib().pkv_pool_create_from_list(int(num_blocks), _iptr(fl), fl.size, ctypes.byref(self._h)))
+
+    def close(self):
+        if self._h:
+            lib().pkv_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int) -> np.ndarray:
+        out = np.empty(max(int(n), 0), dtype=np.int32)
+        _check(lib().pkv_alloc(self._h, int(n), _iptr(out)))
+        return out
+
+    def ref(self, ids) -> None:
+        a = _i32(ids)
+        _check(lib().pkv_ref(self._h, _iptr(a), a.size))
+
+    def free(self, ids) -> None:
+        a = _i32(ids)
+        _check(lib().pkv_free(self._h, _iptr(a), a.size))
+
+    def grow(self, table: np.ndarray, length: int, num_tokens: int) -> int:
+        """Grow int32 `table` (its first `length` entries in use) to cover
+        num_tokens; returns the new length.  Raises PkvError(OUT_OF_BLOCKS)
+        with no change when the free list is short."""
+        if table.dtype != np.int32 or not table.flags.c_contiguous:
+            raise TypeError("table must be a C-contiguous int32 array")
+        n = ctypes.c_int32(int(length))
+        _check(lib().pkv_grow(self._h, _iptr(table), ctypes.byref(n), table.size, int(num_tokens)))
+        return int(n.value)
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pkv_num_free(self._h))
+
+    @property
+    def num_blocks(self) -> int:
+        return int(lib().pkv_num_blocks(self._h))
+
+    def ref_count(self, block_id: int) -> int:
+        return int(lib().pkv_ref_count(self._h, int(block_id)))
+
+    def free_list(self) -> np.ndarray:
+        n = lib().pkv_free_list(self._h, None, 0)
+        out = np.empty(n, dtype=np.int32)
+        lib().pkv_free_list(self._h, _iptr(out), n)
+        return out
+
+
+# ------------------------------------------------------------------ device side
+
+def _stream_ptr(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dptr(t, what: str, dtype_bytes: int | None = None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype_bytes is not None and t.element_size() != dtype_bytes:
+        raise ValueError(f"{what} must have {dtype_bytes}-byte elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class PagedCache:
+    """Descriptor of a caller-owned device KV pool tensor
+    [num_blocks, num_layers, 2, num_heads, 16, 128] of FP16 (or its uint16 bits)."""
+
+    def __init__(self, pool):
+        if pool.dim() != 6 or pool.shape[2] != 2 or pool.shape[4] != BLOCK_SIZE or pool.shape[5] != HEAD_DIM:
+            raise ValueError("pool must be [num_blocks, num_layers, 2, num_heads, 16, 128]")
+        _dptr(pool, "pool", 2)
+        self.pool = pool
+        nb, nl, _, nh, bs, hd = (int(x) for x in pool.shape)
+        self.desc = _lib.PkvCacheDesc(ctypes.c_void_p(pool.data_ptr()), nb, nl, nh, bs, hd)
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.desc.num_heads)
+
+
+def append(cache: PagedCache, layer: int, k_new, v_new, positions, request_of_token, block_tables, stream=None):
+    T = int(positions.numel())
+    R, stride = (int(x) for x in block_tables.shape)
+    _check(lib().pkv_append(ctypes.byref(cache.desc), int(layer), _dptr(k_new, "k_new", 2), _dptr(v_new, "v_new", 2),
+                            _dptr(positions, "positions", 4), _dptr(request_of_token, "request_of_token", 4), T,
+                            _dptr(block_tables, "block_tables", 4), R, stride, _stream_ptr(stream)))
+
+
+def decode_workspace_size(cache: PagedCache, num_rows: int, max_context_len: int) -> int:
+    return int(lib().pkv_decode_workspace_size(ctypes.byref(cache.desc), int(num_rows), int(max_context_len)))
+
+
+def decode_attention(cache: PagedCache, layer: int, out, q, block_tables, context_lens, max_context_len: int,
+                     scale: float, workspace=None, stream=None):
+    R, stride = (int(x) for x in block_tables.shape)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_decode_attention(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2),
+                                      _dptr(block_tables, "block_tables", 4), stride,
+                                      _dptr(context_lens, "context_lens", 4), R, int(max_context_len), float(scale),
+                                      _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+
+
+def prefill_workspace_size(cache: PagedCache, num_rows: int, total_q: int, max_q_per_row: int,
+                           max_context_len: int) -> int:
+    return int(lib().pkv_prefill_workspace_size(ctypes.byref(cache.desc), int(num_rows), int(total_q),
+                                                int(max_q_per_row), int(max_context_len)))
+
+
+def chunked_prefill_attention(cache: PagedCache, layer: int, out, q, query_start, block_tables, context_lens,
+                              max_q_per_row: int, max_context_len: int, scale: float, workspace=None, stream=None):
+    R, stride = (int(x) for x in block_tables.shape)
+    T = int(q.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_chunked_prefill_attention(
+        ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2),
+        _dptr(query_start, "query_start", 4), _dptr(block_tables, "block_tables", 4), stride,
+        _dptr(context_lens, "context_lens", 4), R, T, int(max_q_per_row), int(max_context_len), float(scale),
+        _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))

@@ -1,0 +1,69 @@
+"""ctypes declarations for libpkv.so (the C ABI in include/pkv.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+c_i32 = ctypes.c_int32
+c_i32_p = ctypes.POINTER(ctypes.c_int32)
+c_vp = ctypes.c_void_p
+c_size = ctypes.c_size_t
+
+
+class PkvCacheDesc(ctypes.Structure):
+    _fields_ = [("base", c_vp), ("num_blocks", c_i32), ("num_layers", c_i32), ("num_heads", c_i32),
+                ("block_size", c_i32), ("head_dim", c_i32)]
+
+
+PkvCacheDesc_p = ctypes.POINTER(PkvCacheDesc)
+
+# name -> (restype, argtypes); mirrors include/pkv.h
+SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_pool_create": (ctypes.c_int, [c_i32, ctypes.POINTER(c_vp)]),
+    "pkv_pool_create_from_list": (ctypes.c_int, [c_i32, c_i32_p, c_i32, ctypes.POINTER(c_vp)]),
+    "pkv_pool_destroy": (None, [c_vp]),
+    "pkv_alloc": (ctypes.c_int, [c_vp, c_i32, c_i32_p]),
+    "pkv_ref": (ctypes.c_int, [c_vp, c_i32_p, c_i32]),
+    "pkv_free": (ctypes.c_int, [c_vp, c_i32_p, c_i32]),
+    "pkv_grow": (ctypes.c_int, [c_vp, c_i32_p, c_i32_p, c_i32, c_i32]),
+    "pkv_num_free": (c_i32, [c_vp]),
+    "pkv_num_blocks": (c_i32, [c_vp]),
+    "pkv_ref_count": (c_i32, [c_vp, c_i32]),
+    "pkv_free_list": (c_i32, [c_vp, c_i32_p, c_i32]),
+    "pkv_blocks_needed": (c_i32, [c_i32]),
+    "pkv_append": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp]),
+    "pkv_decode_workspace_size": (c_size, [PkvCacheDesc_p, c_i32, c_i32]),
+    "pkv_decode_attention": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                            ctypes.c_float, c_vp, c_size, c_vp]),
+    "pkv_split_tokens": (c_i32, []),
+    "pkv_prefill_workspace_size": (c_size, [PkvCacheDesc_p, c_i32, c_i32, c_i32, c_i32]),
+    "pkv_chunked_prefill_attention": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
+                                                     c_i32, c_i32, c_i32, c_i32, ctypes.c_float, c_vp, c_size,
+                                                     c_vp]),
+}
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libpkv.so once.  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing; build it with `python -m paged_kv_cache_pkv_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib

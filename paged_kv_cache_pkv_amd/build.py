@@ -1,0 +1,66 @@
+"""Build libpkv.so (host pool + gfx950 HIP kernels) in-tree with hipcc.
+
+    python -m paged_kv_cache_pkv_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libpkv.so")
+OBJDIR = os.path.join(ROOT, "_build", "obj")
+
+SOURCES = ["errors.cpp", "pool.cpp", "append.hip", "decode.hip", "prefill.hip"]
+
+ARCH = "gfx950"
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Packed fp32 VALU forms are kept out of the generated code.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-munsafe-fp-atomics"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}")
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if ln.strip() and noise not in ln]
+    if msgs and verbose:
+        print("\n".join(msgs), flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (always) and link libpkv.so; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(OBJDIR, src + ".o")
+        lang = ["-x", "hip"] + DEVICE if src.endswith(".hip") else ["-x", "c++"]
+        _run([cc, *COMMON, *lang, "-c", path, "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,204 @@
+"""libpkv.so on the CPU: it loads, exports every symbol pkv.h declares, the
+host pool matches the oracle's pool model, and argument validation rejects
+bad calls before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.pool as opool
+import paged_kv_cache_pkv_amd as pkv
+from paged_kv_cache_pkv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 18
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with pkv.h"
+
+
+def test_version_and_constants():
+    assert "gfx950" in pkv.version()
+    assert pkv.split_tokens() % 16 == 0
+    for n, want in ((0, 0), (1, 1), (16, 1), (17, 2), (600, 38), (2300, 144), (8192, 512)):
+        assert pkv.blocks_needed(n) == want == opool.blocks_needed(n)
+
+
+def test_pool_matches_model_fuzz():
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        N = int(rng.integers(1, 300))
+        perm = rng.permutation(N) if trial % 2 else None
+        nfree = N if perm is None else int(rng.integers(0, N + 1))
+        fl = None if perm is None else perm[:nfree]
+        lib_pool = pkv.BlockPool(N, fl)
+        model = opool.BlockPool(N, fl)
+        held = [b for b in range(N) if model.ref[b] > 0]
+        for step in range(400):
+            op = rng.integers(0, 4)
+            if op == 0:
+                n = int(rng.integers(0, 12))
+                try:
+                    want = model.alloc(n)
+                except opool.OutOfBlocks:
+                    with pytest.raises(pkv.PkvError) as e:
+                        lib_pool.alloc(n)
+                    assert e.value.name == "OUT_OF_BLOCKS"
+                else:
+                    got = lib_pool.alloc(n)
+                    assert list(got) == want
+                    held.extend(want)
+            elif op == 1 and held:
+                ids = list(rng.choice(held, size=min(len(held), int(rng.integers(1, 5))), replace=True))
+                try:
+                    model.release(ids)
+                except opool.DoubleFree:
+                    with pytest.raises(pkv.PkvError) as e:
+                        lib_pool.free(ids)
+                    assert e.value.name == "DOUBLE_FREE"
+                else:
+                    lib_pool.free(ids)
+                held = [b for b in range(N) if model.ref[b] > 0]
+            elif op == 2 and held:
+                ids = list(rng.choice(held, size=min(len(held), 3), replace=False))
+                model.share(ids)
+                lib_pool.ref(ids)
+            elif op == 3:
+                b = int(rng.integers(0, N))
+                if model.ref[b] == 0:
+                    with pytest.raises(pkv.PkvError) as e:
+                        lib_pool.free([b])
+                    assert e.value.name == "DOUBLE_FREE"
+            assert lib_pool.num_free == model.num_free()
+            assert list(lib_pool.free_list()) == model.free
+        assert [lib_pool.ref_count(b) for b in range(N)] == model.ref
+        lib_pool.close()
+
+
+def test_pool_pages_arithmetic_and_drain():
+    # the faangrind 7B pool: 7,152 blocks; 73 average (1,550-token) requests fit, 13 at 8,192
+    for tokens, fit in ((1550, 73), (8192, 13)):
+        p = pkv.BlockPool(7152)
+        tables = []
+        while True:
+            try:
+                tables.append(p.alloc(pkv.blocks_needed(tokens)))
+            except pkv.PkvError as e:
+                assert e.name == "OUT_OF_BLOCKS"
+                break
+        assert len(tables) == fit
+        for t in tables:
+            p.free(t)
+        assert p.num_free == 7152  # drain returns every block
+
+
+def test_pool_grow_and_shared_prefix():
+    p = pkv.BlockPool(64, np.random.default_rng(0).permutation(64))
+    t = np.zeros(16, dtype=np.int32)
+    n = p.grow(t, 0, 17)
+    assert n == 2 and p.num_free == 62
+    n = p.grow(t, n, 32)
+    assert n == 2
+    n = p.grow(t, n, 33)
+    assert n == 3
+    with pytest.raises(pkv.PkvError) as e:
+        p.grow(t, n, 16 * 100)
+    assert e.value.name == "INVALID_ARG"  # capacity 16 blocks
+    big = np.zeros(100, dtype=np.int32)
+    with pytest.raises(pkv.PkvError) as e:
+        p.grow(big, 0, 16 * 62)
+    assert e.value.name == "OUT_OF_BLOCKS" and p.num_free == 61
+    # a second row shares the first two blocks
+    p.ref(t[:2])
+    assert p.ref_count(int(t[0])) == 2
+    p.free(t[:3])
+    assert p.ref_count(int(t[0])) == 1 and p.num_free == 62
+    p.free(t[:2])
+    assert p.num_free == 64
+
+
+def test_pool_bad_arguments():
+    with pytest.raises(pkv.PkvError):
+        pkv.BlockPool(0)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.BlockPool(4, [0, 0])
+    assert e.value.name == "BAD_BLOCK"
+    p = pkv.BlockPool(4)
+    with pytest.raises(pkv.PkvError) as e:
+        p.free([7])
+    assert e.value.name == "BAD_BLOCK"
+    with pytest.raises(pkv.PkvError) as e:
+        p.ref([1])
+    assert e.value.name == "DOUBLE_FREE"
+    assert p.ref_count(9) == -1
+
+
+def _desc(**kw):
+    d = dict(base=ctypes.c_void_p(0x100000), num_blocks=64, num_layers=1, num_heads=32, block_size=16, head_dim=128)
+    d.update(kw)
+    return _lib.PkvCacheDesc(d["base"], d["num_blocks"], d["num_layers"], d["num_heads"], d["block_size"],
+                             d["head_dim"])
+
+
+FAKE = ctypes.c_void_p(0x200000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), -2), (dict(block_size=32), -2), (dict(num_heads=0), -2),
+    (dict(base=ctypes.c_void_p(0)), -1), (dict(num_layers=0), -1),
+])
+def test_validation_cache(kw, code):
+    L = pkv.lib()
+    d = _desc(**kw)
+    rc = L.pkv_decode_attention(ctypes.byref(d), 0, FAKE, FAKE, FAKE, 16, FAKE, 4, 256, 0.088, FAKE, 1 << 20, None)
+    assert rc == code
+    assert L.pkv_last_error()
+    rc = L.pkv_append(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, 16, None)
+    assert rc == code
+
+
+def test_validation_decode_args():
+    L = pkv.lib()
+    d = _desc()
+    args = lambda **k: dict(dict(layer=0, out=FAKE, q=FAKE, bt=FAKE, stride=16, cl=FAKE, R=4, maxL=256, scale=0.088,
+                                 ws=FAKE, wsb=1 << 20), **k)
+    def call(a):
+        return L.pkv_decode_attention(ctypes.byref(d), a["layer"], a["out"], a["q"], a["bt"], a["stride"], a["cl"],
+                                      a["R"], a["maxL"], a["scale"], a["ws"], a["wsb"], None)
+    assert call(args(layer=1)) == -1
+    assert call(args(R=0)) == -1
+    assert call(args(maxL=0)) == -1
+    assert call(args(maxL=16 * 16 + 1)) == -1
+    assert call(args(out=None)) == -1
+    assert call(args(scale=float("nan"))) == -1
+    assert call(args(scale=-1.0)) == -1
+    assert call(args(q=ctypes.c_void_p(0x200002))) == -1  # misaligned
+    need = L.pkv_decode_workspace_size(ctypes.byref(d), 4, 4096)
+    assert need > 0
+    assert call(args(stride=256, maxL=4096, ws=None)) == -6
+    assert call(args(stride=256, maxL=4096, wsb=need - 1)) == -6
+    assert call(args(stride=256, maxL=4096, ws=ctypes.c_void_p(0x200010), wsb=need)) == -6  # 256-B alignment
+
+
+def test_validation_append_args():
+    L = pkv.lib()
+    d = _desc()
+    assert L.pkv_append(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 4, 16, None) == 0  # empty = no-op
+    assert L.pkv_append(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 4, 16, None) == -1
+    assert L.pkv_append(ctypes.byref(d), 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, 16, None) == -1
+    assert L.pkv_append(ctypes.byref(d), 0, None, FAKE, FAKE, FAKE, 4, FAKE, 4, 16, None) == -1
+    assert L.pkv_append(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 16, None) == -1
