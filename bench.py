@@ -36,6 +36,33 @@ LAYER_TOKEN_BYTES = 2 * 32 * 128 * 2          # K+V of one token, one layer
 STEP_TOKEN_BYTES = LAYER_TOKEN_BYTES * 32       # all 32 layers
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "decode_average_mix_hbm_counters.json")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_pkv_amd", "csrc", n) for n in ("decode.hip", "device_common.h")]
+
+
+def source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when the decode kernel source has changed since it was taken."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,6 +72,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times (a known-size kernel for "
+                         "calibrating HBM byte counters)")
     return ap.parse_args()
 
 
@@ -117,6 +147,9 @@ def main():
         slab = pool_d[torch.from_numpy(ids.astype(np.int64)).to(dev), 0].cpu().numpy().view(np.uint16)
         cpu_sample = (ids, slab)
 
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
     def host_step(k):
         """Grow tables for this step's new token, stage the upload."""
         lens = lens0 + k
@@ -133,24 +166,26 @@ def main():
         pos_d.copy_(buf[R * stride + R:], non_blocking=True)
         return int(lens.sum())
 
-    def events(n):
-        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    # Per-launch timing: two decode launches per timed step carry HIP events
+    # (layers rotate so every layer is sampled); bracketing all 32 would add
+    # about 5% to the step.
+    samples = []  # (step index, layer, start event, end event)
+    spare_events = events(4 * args.steps)
 
-    # one (start, end) event pair per timed (step, layer) launch
-    ev_app = [(events(NL), events(NL)) for _ in range(args.steps)]
-    ev_dec = [(events(NL), events(NL)) for _ in range(args.steps)]
+    def sampled_layers(i):
+        return {(2 * i) % NL, (2 * i + NL // 2) % NL}
 
     def gpu_step(i):
+        pick = sampled_layers(i) if i is not None else ()
         for l in range(NL):
-            if i is not None:
-                ev_app[i][0][l].record(stream)
             pkv.append(cache, l, k_d[l], v_d[l], pos_d, rot_d, tables_d, stream=stream)
-            if i is not None:
-                ev_app[i][1][l].record(stream)
-                ev_dec[i][0][l].record(stream)
+            if l in pick:
+                e0, e1 = spare_events.pop(), spare_events.pop()
+                e0.record(stream)
             pkv.decode_attention(cache, l, out_d[l], q_d[l], tables_d, lens_d, max_ctx, SCALE, ws_d, stream=stream)
-            if i is not None:
-                ev_dec[i][1][l].record(stream)
+            if l in pick:
+                e1.record(stream)
+                samples.append((i, l, e0, e1))
 
     log(args, f"rows={R} sum_context={int(lens0.sum())} max_context={int(lens0.max())} ws={ws_bytes}")
     parity = None
@@ -166,13 +201,11 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     tokens = 0
-    dec_bytes = 0
     t_start.record(stream)
     wall0 = time.perf_counter()
     for i, k in enumerate(range(args.warmup, total_steps)):
         step_tokens = host_step(k)
         tokens += step_tokens
-        dec_bytes += step_tokens * LAYER_TOKEN_BYTES * NL
         gpu_step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -180,12 +213,12 @@ def main():
     elapsed_ms = t_start.elapsed_time(t_end)
     log(args, f"timed {args.steps} steps: {elapsed_ms:.2f} ms (wall {wall * 1e3:.1f} ms)")
 
-    dec_all = [ev_dec[i][0][l].elapsed_time(ev_dec[i][1][l]) for i in range(args.steps) for l in range(NL)]
-    app_all = [ev_app[i][0][l].elapsed_time(ev_app[i][1][l]) for i in range(args.steps) for l in range(NL)]
-    dec_avg_ms = float(np.mean(dec_all))
-    bytes_per_decode = dec_bytes / (args.steps * NL)
+    dec_ms = [e0.elapsed_time(e1) for (_, _, e0, e1) in samples]
+    dec_avg_ms = float(np.mean(dec_ms))
+    bytes_per_decode = float(np.mean([int((lens0 + args.warmup + i).sum()) * LAYER_TOKEN_BYTES
+                                      for (i, _, _, _) in samples]))
     achieved = bytes_per_decode / (dec_avg_ms / 1e3) / 1e9
-    app_avg_us = float(np.mean(app_all)) * 1e3
+    traffic = counted_traffic()
 
     ms_per_step = elapsed_ms / args.steps
     value = tokens / (elapsed_ms / 1e3)
@@ -216,7 +249,7 @@ def main():
         t0 = time.perf_counter()
         rows_done = tok_done = bad = 0
         max_abs = 0.0
-        while time.perf_counter() - t0 < args.cpu_seconds and rows_done < 4 * R:
+        while time.perf_counter() - t0 < args.cpu_seconds and rows_done < 64 * R:
             r = rows_done % R
             ref = opaged.decode(Blocks(), batch.q[0], tbl0, lens0, SCALE, rows=[r])[0]
             rows_done += 1
@@ -254,16 +287,25 @@ def main():
         "hbm_tb_s": value * STEP_TOKEN_BYTES / 1e12,
         "hbm_frac_of_peak": value * STEP_TOKEN_BYTES / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "pkv_decode_attention (split + merge launches), one layer",
                      "avg_launch_ms": dec_avg_ms, "bytes_per_launch": bytes_per_decode,
-                     "launches": len(dec_all)},
-        "append_avg_us": app_avg_us,
+                     "launches_timed": len(dec_ms)},
         "wall_s_timed": wall,
         "parity_step0_layer0": parity,
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(rec), flush=True)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(args, f"copy probe: 3 x {args.copy_probe_mib} MiB device-to-device copies done")
 
 
 if __name__ == "__main__":

@@ -19,36 +19,66 @@
 // l/16, l/16 + 4, l/16 + 8, l/16 + 12: every load instruction moves four
 // whole 256-byte token rows (1 KiB contiguous per wave), straight into
 // registers -- each lane consumes exactly what it loads, so no LDS staging is
-// needed.  Scores are dot products of FP16 pairs accumulated in fp32
+// needed.  Loads carry the non-temporal cache policy.  Scores are dot products of FP16 pairs accumulated in fp32
 // (v_dot2_f32_f16), summed over the 16 lanes of a token with DPP moves.  Each
 // group of 16 lanes keeps its own online-softmax state over its four tokens
 // of every block; the four groups merge once at the end of the range.  Blocks
-// are software-pipelined one ahead so a wave keeps 16 KiB in flight.
+// are software-pipelined two ahead so a wave keeps 24 KiB in flight.
 
 #include "device_common.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kSplitBlocks = 32;  // 512 tokens per range
-constexpr int kWavesPerGroup = 4;  // heads per workgroup
+// Tunables (compile-time; the split size must stay fixed for a given build so
+// that a row's result never depends on its batch neighbours).
+#ifndef PKV_SPLIT_BLOCKS
+#define PKV_SPLIT_BLOCKS 16
+#endif
+#ifndef PKV_PREFETCH
+#define PKV_PREFETCH 2
+#endif
+#ifndef PKV_XCD_REMAP
+#define PKV_XCD_REMAP 1
+#endif
+// Cache-policy bits of the K/V buffer loads: 2 = nt (streaming).  Keys and
+// values are read once per step, and on gfx950 the non-temporal policy lifts
+// the scattered-slab read rate from ~5.2 to ~6.5 TB/s.
+#ifndef PKV_MIN_WAVES
+#define PKV_MIN_WAVES 1
+#endif
+#ifndef PKV_KV_CPOL
+#define PKV_KV_CPOL 2
+#endif
+#ifndef PKV_WAVES
+#define PKV_WAVES 8
+#endif
+
+constexpr int kSplitBlocks = PKV_SPLIT_BLOCKS;  // blocks per split-K range
+constexpr int kWavesPerGroup = PKV_WAVES;       // heads per workgroup
 constexpr int kDecodeThreads = 64 * kWavesPerGroup;
+constexpr int kDepth = PKV_PREFETCH + 1;        // tiles held in registers
+constexpr int kXcds = 8;
+static_assert(kSplitBlocks >= 1 && kSplitBlocks <= 64, "a range's block ids must fit one wave");
 
 struct KVTile {
   uint4 k[4];
   uint4 v[4];
 };
 
-__device__ __forceinline__ void load_tile(KVTile& t, const uint16_t* __restrict__ kslab,
-                                          const uint16_t* __restrict__ vslab, int lane_off) {
+// Load one block's K and V rows for this lane through a buffer resource that
+// spans the head's K tile up to the end of its V tile (vdelta bytes apart);
+// the resource's range check turns any stray offset into a zero read.
+__device__ __forceinline__ void load_tile(KVTile& t, const uint16_t* __restrict__ kslab, int vdelta, int lane_off) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kslab), 0, vdelta + kBlockSize * kHeadDim * 2, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    t.k[i] = *reinterpret_cast<const uint4*>(kslab + lane_off + i * 4 * kHeadDim);
-  }
+  for (int i = 0; i < 4; ++i)
+    t.k[i] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(rs, (lane_off + i * 4 * kHeadDim) * 2, 0, PKV_KV_CPOL));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    t.v[i] = *reinterpret_cast<const uint4*>(vslab + lane_off + i * 4 * kHeadDim);
-  }
+  for (int i = 0; i < 4; ++i)
+    t.v[i] = bitcast<uint4>(
+        __builtin_amdgcn_raw_buffer_load_b128(rs, vdelta + (lane_off + i * 4 * kHeadDim) * 2, 0, PKV_KV_CPOL));
 }
 
 struct SoftmaxState {
@@ -126,10 +156,25 @@ struct DecodeArgs {
   float qk_scale;       // scale * log2(e)
 };
 
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs a) {
-  const int split = blockIdx.x;
-  const int r = blockIdx.y;
-  const int h = blockIdx.z * kWavesPerGroup + (threadIdx.x >> 6);
+__global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_kernel(DecodeArgs a) {
+  // 1-D grid over (row, range, head group).  Workgroups go to the XCDs
+  // round-robin by index; with the remap, the head groups of one (row,
+  // range) land on one XCD back to back, so they share its L2 and TLB for
+  // the same block slabs.
+  const int head_groups = (a.num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int n = blockIdx.x;
+#if PKV_XCD_REMAP
+  const int m = n / kXcds;
+  const int hg = m % head_groups;
+  const int rs = (n % kXcds) + kXcds * (m / head_groups);
+#else
+  const int hg = n % head_groups;
+  const int rs = n / head_groups;
+#endif
+  const int split = rs % a.max_splits;
+  const int r = rs / a.max_splits;
+  if (r >= a.num_rows) return;
+  const int h = hg * kWavesPerGroup + (threadIdx.x >> 6);
   if (h >= a.num_heads) return;
   const int lane = threadIdx.x & 63;
   const int group = lane >> 4;  // token within each 4-token stripe
@@ -165,23 +210,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
     return id;
   };
   auto slab_k = [&](int id) { return a.pool + slab_offset(id, a.layer, 0, h, a.num_layers, a.num_heads); };
-  auto slab_v = [&](int id) { return a.pool + slab_offset(id, a.layer, 1, h, a.num_layers, a.num_heads); };
+  const int vdelta = a.num_heads * kBlockSize * kHeadDim * 2;  // bytes from a head's K tile to its V tile
 
-  KVTile cur, nxt;
-  int id = block_id(b0);
-  bool ok = (unsigned)id < (unsigned)a.num_blocks;
-  load_tile(cur, slab_k(ok ? id : 0), slab_v(ok ? id : 0), lane_off);
-  for (int j = b0; j < b1; ++j) {
-    bool ok_next = false;
-    if (j + 1 < b1) {
-      const int idn = block_id(j + 1);
-      ok_next = (unsigned)idn < (unsigned)a.num_blocks;
-      load_tile(nxt, slab_k(ok_next ? idn : 0), slab_v(ok_next ? idn : 0), lane_off);
+  // Software pipeline: block j + kDepth - 1 is loading while block j is folded.
+  KVTile tile[kDepth];
+  bool ok[kDepth];
+  auto issue = [&](KVTile& t, bool& good, int j) {
+    const int id = block_id(j);
+    good = (unsigned)id < (unsigned)a.num_blocks;
+    const int safe = good ? id : 0;
+    load_tile(t, slab_k(safe), vdelta, lane_off);
+  };
+#pragma unroll
+  for (int u = 0; u < kDepth - 1; ++u)
+    if (b0 + u < b1) issue(tile[u], ok[u], b0 + u);
+  for (int j = b0; j < b1; j += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int jj = j + u;
+      constexpr int kAhead = kDepth - 1;
+      if (jj + kAhead < b1) issue(tile[(u + kAhead) % kDepth], ok[(u + kAhead) % kDepth], jj + kAhead);
+      if (jj < b1) {
+        const int valid = ok[u] ? min(L - jj * kBlockSize, kBlockSize) : 0;
+        fold_tile(st, tile[u], q, a.qk_scale, group, valid);
+      }
     }
-    const int valid = ok ? min(L - j * kBlockSize, kBlockSize) : 0;
-    fold_tile(st, cur, q, a.qk_scale, group, valid);
-    cur = nxt;
-    ok = ok_next;
   }
   merge_groups(st);
 
@@ -207,8 +260,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
 }
 
 // Merge the ranges of every (row, head) that has more than one.  One wave per
-// (row, head); lane l owns dims 2l, 2l+1.  Ranges are combined in index order,
-// so the result does not depend on which range finished first.
+// (row, head).  Lane s holds range s's statistics, so the maximum and the
+// weights w_s = exp2(m_s - M) come from one parallel load and a wave
+// reduction; lane l then owns dims 2l, 2l+1 and accumulates w_s * o_s over the
+// ranges in index order (independent loads, unrolled), so the result does not
+// depend on which range finished first.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
 __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeArgs a) {
   const int r = blockIdx.x;
   const int h = blockIdx.y * kWavesPerGroup + (threadIdx.x >> 6);
@@ -222,16 +284,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeArgs
   if (nsplit <= 1) return;
   const size_t rh = (size_t)r * a.num_heads + h;
   const float2* ml = a.part_ml + rh * a.max_splits;
+  const float2* po = reinterpret_cast<const float2*>(a.part_o + rh * a.max_splits * kHeadDim) + lane;
+
   float M = kMinusBig;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[s].x);
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int s = s0 + lane;
+    M = fmaxf(M, s < nsplit ? ml[s].x : kMinusBig);
+  }
+  M = wave_max(M);
   float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ms = ml[s];
-    const float w = fast_exp2(ms.x - M);
-    l = fmaf(ms.y, w, l);
-    const float2 po = reinterpret_cast<const float2*>(a.part_o + (rh * a.max_splits + s) * kHeadDim)[lane];
-    o0 = fmaf(po.x, w, o0);
-    o1 = fmaf(po.y, w, o1);
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int s = s0 + lane;
+    const float2 mine = s < nsplit ? ml[s] : make_float2(kMinusBig, 0.0f);
+    const float w_mine = fast_exp2(mine.x - M);
+    const int n = min(64, nsplit - s0);
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+      float2 p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p[u] = po[(size_t)(s0 + j + u) * (kHeadDim / 2)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), j + u));
+        o0 = fmaf(p[u].x, w, o0);
+        o1 = fmaf(p[u].y, w, o1);
+      }
+    }
+    for (; j < n; ++j) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), j));
+      const float2 p = po[(size_t)(s0 + j) * (kHeadDim / 2)];
+      o0 = fmaf(p.x, w, o0);
+      o1 = fmaf(p.y, w, o1);
+    }
+    // l = sum_s l_s w_s over this chunk, added in index order
+    for (int jj = 0; jj < n; ++jj) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), jj));
+      const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.y), jj));
+      l = fmaf(ls, w, l);
+    }
   }
   const float inv = 1.0f / l;
   reinterpret_cast<uint32_t*>(a.out)[rh * 64 + lane] = pack_half2(o0 * inv, o1 * inv);
@@ -299,7 +389,13 @@ extern "C" int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void*
   a.qk_scale = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int head_groups = (cache->num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
-  decode_split_kernel<<<dim3(ms, num_rows, head_groups), dim3(kDecodeThreads), 0, s>>>(a);
+  int64_t rs_total = (int64_t)num_rows * ms;
+#if PKV_XCD_REMAP
+  rs_total = (rs_total + kXcds - 1) / kXcds * kXcds;
+#endif
+  const int64_t wgs = rs_total * head_groups;
+  if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  decode_split_kernel<<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
   if (int rc = check_launch("decode split kernel")) return rc;
   if (ms > 1) {
     decode_merge_kernel<<<dim3(num_rows, head_groups), dim3(kDecodeThreads), 0, s>>>(a);
