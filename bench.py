@@ -37,7 +37,7 @@ STEP_TOKEN_BYTES = LAYER_TOKEN_BYTES * 32       # all 32 layers
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "decode_average_mix_hbm_counters.json")
-DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_pkv_amd", "csrc", n) for n in ("decode.hip", "device_common.h")]
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_pkv_amd", "csrc", n) for n in ("decode.hip", "decode_core.h", "device_common.h")]
 
 
 def source_digest() -> str:
