@@ -63,6 +63,77 @@ def counted_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(batch) -> float:
+    """Causal (query, key) pairs of the rows with at least two queries x 4 x D x H."""
+    total = 0
+    for r in range(batch.rows):
+        n = int(batch.q_counts[r])
+        L = int(batch.context_lens[r])
+        if n >= 2:
+            total += n * (L - n + 1) + n * (n - 1) // 2  # sum over i < n of (L - n + i + 1)
+    return 4.0 * 128 * batch.num_heads * total
+
+
+def measure_prefill(torch, pkv, dev, stream, reps=20):
+    """Chunked prefill on MFMA: a 512-token chunk at offset 7,488 of an 8,000-token
+    prompt, alone and mixed with 31 average-mix decode rows in one launch,
+    over a one-layer 7,152-block pool.  Returns a dict for the JSON line."""
+    from workloads import SCALE, build_batch, c5_mixed, fill_normal_fp16_device
+
+    pool = torch.empty((7152, 1, 2, 32, 16, 128), dtype=torch.int16, device=dev)
+    fill_normal_fp16_device(pool, seed=2004)
+    cache = pkv.PagedCache(pool)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    def timed(batch):
+        tables, qs, lens = d(batch.block_tables), d(batch.query_start), d(batch.context_lens)
+        q, k, v = d(batch.q[0]), d(batch.k_new[0]), d(batch.v_new[0])
+        pos, rot = d(batch.positions), d(batch.request_of_token)
+        T, maxq, maxL = batch.total_q, int(batch.q_counts.max()), int(batch.context_lens.max())
+        ws = torch.empty(pkv.prefill_workspace_size(cache, batch.rows, T, maxq, maxL), dtype=torch.uint8, device=dev)
+        out = torch.empty((T, 32, 128), dtype=torch.float16, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        pkv.append(cache, 0, k, v, pos, rot, tables, stream=stream)
+        pkv.chunked_prefill_attention(cache, 0, out, q, qs, tables, lens, maxq, maxL, SCALE, ws, stream=stream)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            pkv.append(cache, 0, k, v, pos, rot, tables, stream=stream)
+        ev[1].record(stream)
+        for _ in range(reps):
+            pkv.chunked_prefill_attention(cache, 0, out, q, qs, tables, lens, maxq, maxL, SCALE, ws, stream=stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
+
+    mixed = c5_mixed(with_pool=False)
+    chunk = build_batch("chunk-only", 4, [8000], [512], num_blocks=7152, with_pool=False, stride=520)
+    app_mixed_ms, mixed_ms = timed(mixed)
+    _, chunk_ms = timed(chunk)
+    flops = prefill_flops(chunk)
+    kv_mixed = float(mixed.context_lens.sum()) * LAYER_TOKEN_BYTES
+    tflops = flops / (chunk_ms / 1e3) / 1e12
+    return {
+        "workload": "512-token causal chunk at offset 7488 of an 8000-token prompt + 31 average-mix decode rows, "
+                    "one layer, 32 heads x 128, FP16",
+        "mixed_launch_us": mixed_ms * 1e3,
+        "mixed_kv_bytes": kv_mixed,
+        "mixed_hbm_gb_s": kv_mixed / (mixed_ms / 1e3) / 1e9,
+        "chunk_only_launch_us": chunk_ms * 1e3,
+        "chunk_flops": flops,
+        "append_543_tokens_us": app_mixed_ms * 1e3,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "pkv_chunked_prefill_attention on the chunk alone (tile + merge launches)"},
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,6 +143,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a known-size kernel for "
                          "calibrating HBM byte counters)")
@@ -266,6 +338,10 @@ def main():
                         "sample": f"fp64 oracle decode of {rows_done} (row, layer-0) tasks of the same step, "
                                   f"{tok_done} one-layer tokens in {cpu_s:.1f} s; value = layer-tokens / 32 / s"}
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = measure_prefill(torch, pkv, dev, stream)
+
     rec = {
         "metric": METRIC,
         "value": value,
@@ -293,6 +369,7 @@ def main():
                      "launches_timed": len(dec_ms)},
         "wall_s_timed": wall,
         "parity_step0_layer0": parity,
+        "prefill": prefill,
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(rec), flush=True)

@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_ke
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
-  const int h = hg * kWavesPerGroup + (threadIdx.x >> 6);
+  // wave-uniform: lets every address derived from the head live in scalar registers
+  const int h = __builtin_amdgcn_readfirstlane(hg * kWavesPerGroup + (threadIdx.x >> 6));
   if (h >= a.num_heads) return;
 
   int L = a.context_lens[r];
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_ke
 // (row, head).
 __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeArgs a) {
   const int r = blockIdx.x;
-  const int h = blockIdx.y * kWavesPerGroup + (threadIdx.x >> 6);
+  const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kWavesPerGroup + (threadIdx.x >> 6));
   if (h >= a.num_heads) return;
   int L = a.context_lens[r];
   L = L > a.max_context_len ? a.max_context_len : L;

@@ -9,15 +9,16 @@
 // request (LLM inference batching, faangrind, "Prefill and decode share each
 // step"), so one launch serves both.
 //
-// Prefill tiles (rows with n >= 2).  A workgroup of 4 waves owns 128 queries
+// Prefill tiles (rows with n >= 2).  A workgroup of 8 waves owns 256 queries
 // of one head and one fixed range of kPrefillSplit keys; wave w owns 32
-// queries.  Keys advance 64 at a time (four 16-token blocks gathered through
-// the block table) and are staged in LDS: K as [key][dim], V transposed as
-// [dim][key] with the key order inside each group of 16 bit-swapped (bits 2
-// and 3) so that the MFMA operand of P*V is one 16-byte LDS read.  On
+// queries.  Keys advance 64 at a time: four 16-token blocks gathered through
+// the block table by direct global->LDS loads (no registers), four LDS stages
+// deep so the loads run three steps ahead of the matrix cores.  K and V sit in
+// LDS row-major; V reaches the MFMA transposed through ds_read_b64_tr_b16.  On
 // v_mfma_f32_32x32x16_f16:
 //   S^T = K Q^T      A = K rows from LDS, B = the wave's queries (registers)
-//   O^T += V^T P^T   A = V^T rows from LDS, B = P straight from S^T's registers
+//   O^T += V^T P^T   A = V^T via transposed LDS reads, B = P straight from
+//                    S^T's registers
 // In S^T's accumulator layout every query's 64 scores sit in two lanes
 // (l and l ^ 32), so the softmax row maximum is one cross-lane exchange.  The
 // online-softmax statistics combine across key steps and across ranges
@@ -29,36 +30,69 @@
 // head and 256-token range).  A merge launch combines the ranges of every
 // query that has more than one.
 
+#include <type_traits>
+
 #include "decode_core.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kPrefillThreads = 256;
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4
+#endif
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 2
+#endif
+constexpr int kPrefillThreads = 64 * PKV_PREFILL_WAVES;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kQPerWave = 32;
 constexpr int kBQ = kPrefillWaves * kQPerWave;  // queries per tile
 constexpr int kBK = 64;                         // keys per step
+#ifndef PKV_PREFILL_INTERLEAVE
+#define PKV_PREFILL_INTERLEAVE 0
+#endif
 #ifndef PKV_PREFILL_SPLIT
 #define PKV_PREFILL_SPLIT 2048
 #endif
 constexpr int kPrefillSplit = PKV_PREFILL_SPLIT;  // keys per range
 static_assert(kPrefillSplit % kBK == 0, "ranges hold whole key steps");
-constexpr int kKRow = kHeadDim * 2 + 16;   // LDS bytes per K row (padded)
-constexpr int kVRow = kBK * 2 + 16;        // LDS bytes per V^T row (padded)
-constexpr int kKBytes = kBK * kKRow;
-constexpr int kVBytes = kHeadDim * kVRow;
-constexpr int kLdsBytes = kKBytes + kVBytes;
+static_assert(kPrefillSplit / kBK <= 64, "a range's block ids for one slot fit one wave");
+constexpr int kRowBytes = kHeadDim * 2;        // one key's 128 dims
+constexpr int kTileBytes = kBK * kRowBytes;     // K (or V) of one step: 16 KiB
+constexpr int kStageBytes = 2 * kTileBytes;     // K tile then V tile
 constexpr int kXcds = 8;
+constexpr int kStages = PKV_PREFILL_STAGES;  // LDS stages: direct loads run kStages - 1 steps ahead
+static_assert(kStages == 2 || kStages == 4, "2 or 4 LDS stages");
+static_assert(kPrefillWaves == 4 || kPrefillWaves == 8, "4 or 8 waves per tile");
+// direct loads each wave issues per step: with 4 waves a wave gathers one
+// block's K and V (8 loads), with 8 waves one block's K or V (4 loads)
+constexpr int kLoadsPerStep = kPrefillWaves == 4 ? 8 : 4;
 
-// V^T rows hold 8 chunks of 16 bytes (8 key positions each).  Chunk c of row d
-// is stored at chunk c ^ ((d >> 3) & 7): the 16 rows a store instruction hits
-// then fall in different banks instead of all in one (144-byte rows repeat
-// every 8 rows modulo the bank count).
-__device__ __forceinline__ int vt_offset(int d, int pos) {
-  const int chunk = (pos >> 3) ^ ((d >> 3) & 7);
-  return d * kVRow + chunk * 16 + (pos & 7) * 2;
+// Two LDS stages, as distinct objects so that the compiler can tell the stage
+// being filled by direct loads from the stage being read.  Rows are 256 bytes
+// (16 chunks of 16 bytes, no padding); chunk c of tile row r is stored at
+// position c ^ swz(r), swz swapping the two 2-bit halves of r & 15.  Then the
+// 16 consecutive rows of one K operand read land on 16 distinct positions, and
+// so do the 4 rows x 4 chunks of one transposed V read: both are free of bank
+// conflicts.
+__shared__ __attribute__((aligned(16))) char g_prefill_stage0[kStageBytes];
+__shared__ __attribute__((aligned(16))) char g_prefill_stage1[kStageBytes];
+#if PKV_PREFILL_STAGES == 4
+__shared__ __attribute__((aligned(16))) char g_prefill_stage2[kStageBytes];
+__shared__ __attribute__((aligned(16))) char g_prefill_stage3[kStageBytes];
+#endif
+
+template <int S>
+__device__ __forceinline__ char* prefill_stage() {
+#if PKV_PREFILL_STAGES == 4
+  return S == 0 ? g_prefill_stage0 : S == 1 ? g_prefill_stage1 : S == 2 ? g_prefill_stage2 : g_prefill_stage3;
+#else
+  return S == 0 ? g_prefill_stage0 : g_prefill_stage1;
+#endif
 }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define PKV_LDS __attribute__((address_space(3)))
 
 struct PrefillArgs {
   const uint16_t* pool;
@@ -72,7 +106,8 @@ struct PrefillArgs {
   int layer, num_blocks, num_layers, num_heads;
   int bt_stride, num_rows, total_q, max_context_len, max_splits;
   int tiles_max, ranges_max;   // prefill grid factors
-  int prefill_wgs;             // workgroups [0, prefill_wgs) are prefill tiles (a multiple of kXcds)
+  int prefill_wgs;             // prefill tile workgroups (a multiple of kXcds)
+  int decode_wgs;              // decode workgroups (a multiple of kXcds)
   float qk_scale;              // scale * log2(e)
 };
 
@@ -119,9 +154,95 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ h8 as_h8(const uint4& v) { return bitcast<h8>(v); }
 
-__device__ void prefill_tile(const PrefillArgs& a, int r, int qtile, int h, int kr, char* __restrict__ lds) {
+// Wait for this wave's outstanding direct loads, then a workgroup barrier;
+// the empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+struct TileCtx {
+  int ids;                  // lane i: block id of step i for this wave's block slot (or -1)
+  const uint16_t* k_head;   // K tile of head h in block 0 of the layer
+  size_t block_stride;      // elements between blocks
+  size_t vdelta;            // elements from a head's K tile to its V tile
+  int nb, L, num_blocks;
+  int voff[4];              // this lane's source byte offsets for the 4 row quads of a block
+};
+
+// Each step gathers four 16-token blocks (kb / 16 + b, b = 0..3).  With 4
+// waves, wave b loads block b's K rows and then its V rows; with 8 waves,
+// waves 0-3 load the K rows and waves 4-7 the V rows.  Every load is a direct
+// 1 KiB global->LDS transfer in which each lane fetches the chunk that the
+// swizzle puts in its LDS slot.  The buffer resource covers only the block's
+// live rows, so rows past the context (and whole blocks with an invalid id)
+// read as zero.
+template <int S>
+__device__ __forceinline__ void issue_half(const TileCtx& c, int kb, int step, int blk, bool is_v) {
+  const int first = kb + kBlockSize * blk;
+  int rows = c.L - first;
+  rows = rows < 0 ? 0 : (rows > kBlockSize ? kBlockSize : rows);
+  const int id = __builtin_amdgcn_readlane(c.ids, step);
+  const bool ok = (unsigned)id < (unsigned)c.num_blocks && rows > 0;
+  // block id and row count are wave-uniform; keep the resource words scalar
+  const uint16_t* base =
+      uniform_ptr(c.k_head + (ok ? (size_t)id * c.block_stride : 0) + (is_v ? c.vdelta : 0));
+  const int nrec = __builtin_amdgcn_readfirstlane(ok ? rows * kRowBytes : 0);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, nrec, 0x00020000);
+  char* dst = prefill_stage<S>() + (is_v ? kTileBytes : 0) + kBlockSize * blk * kRowBytes;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PKV_LDS void*)(dst + 4 * q * kRowBytes), 16, c.voff[q], 0, 0, 0);
+}
+
+template <int S>
+__device__ __forceinline__ void issue_step(const TileCtx& c, int kb, int step) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (kPrefillWaves == 4) {
+    issue_half<S>(c, kb, step, wave, false);
+    issue_half<S>(c, kb, step, wave, true);
+  } else {
+    issue_half<S>(c, kb, step, wave & 3, wave >= 4);
+  }
+}
+
+// Wait until at most `ahead` later steps' loads are outstanding for this wave,
+// then synchronise the workgroup.
+__device__ __forceinline__ void stage_wait(int ahead) {
+  if (ahead >= 2) {
+    if (kLoadsPerStep == 8) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else if (ahead == 1) {
+    if (kLoadsPerStep == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h_in, int kr_in) {
+  // the tile coordinates are workgroup-uniform; say so, so that block ids and
+  // buffer resources stay in scalar registers
+  const int r = __builtin_amdgcn_readfirstlane(r_in);
+  const int qtile = __builtin_amdgcn_readfirstlane(qtile_in);
+  const int h = __builtin_amdgcn_readfirstlane(h_in);
+  const int kr = __builtin_amdgcn_readfirstlane(kr_in);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;   // query column of this lane in the wave's 32
   const int half = lane >> 5;  // which 8 of each 16 reduction elements the lane holds
@@ -144,6 +265,40 @@ __device__ void prefill_tile(const PrefillArgs& a, int r, int qtile, int h, int 
   const int p_wave_last = wq0 < q_end ? L - n + min(q_end, wq0 + kQPerWave) - 1 : -1;
   const int p_wave_first = L - n + wq0;
 
+  TileCtx c;
+  {
+    // one load brings every step's block id for this wave's block slot
+    const int32_t* row_table = a.block_tables + (size_t)r * a.bt_stride;
+    const int nb = (L + kBlockSize - 1) / kBlockSize;
+    const int j = k_begin / kBlockSize + 4 * lane + (kPrefillWaves == 4 ? wave : (wave & 3));
+    c.ids = (lane < kPrefillSplit / kBK && j < nb) ? row_table[j] : -1;
+  }
+  c.block_stride = (size_t)a.num_layers * 2 * a.num_heads * kBlockSize * kHeadDim;
+  c.vdelta = (size_t)a.num_heads * kBlockSize * kHeadDim;
+  c.k_head = a.pool + slab_offset(0, a.layer, 0, h, a.num_layers, a.num_heads);
+  c.nb = (L + kBlockSize - 1) / kBlockSize;
+  c.L = L;
+  c.num_blocks = a.num_blocks;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 4 * q + (lane >> 4);  // row of the block this lane's slot holds
+    const int chunk = (lane & 15) ^ swz(row);  // the chunk the swizzle puts in slot lane & 15
+    c.voff[q] = row * kRowBytes + chunk * 16;
+  }
+
+  // Stale LDS from earlier workgroups must never meet a zero weight as NaN.
+  {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < kStageBytes / 16; i += kPrefillThreads) {
+      reinterpret_cast<uint4*>(g_prefill_stage0)[i] = z;
+      reinterpret_cast<uint4*>(g_prefill_stage1)[i] = z;
+#if PKV_PREFILL_STAGES == 4
+      reinterpret_cast<uint4*>(g_prefill_stage2)[i] = z;
+      reinterpret_cast<uint4*>(g_prefill_stage3)[i] = z;
+#endif
+    }
+  }
+
   // The wave's queries as MFMA B operands: Q[wq][16k + 8*half .. +7], k = 0..7.
   h8 qf[8];
   {
@@ -162,69 +317,37 @@ __device__ void prefill_tile(const PrefillArgs& a, int r, int qtile, int h, int 
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m = kMinusBig, lsum = 0.0f;
 
-  const int32_t* row_table = a.block_tables + (size_t)r * a.bt_stride;
-  const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const size_t block_stride = (size_t)a.num_layers * 2 * a.num_heads * kBlockSize * kHeadDim;
-  const uint16_t* k_head = a.pool + slab_offset(0, a.layer, 0, h, a.num_layers, a.num_heads);
-  const uint16_t* v_head = a.pool + slab_offset(0, a.layer, 1, h, a.num_layers, a.num_heads);
+  // Per-lane LDS offsets.  K operand (S^T = K Q^T): row 32T + col, chunk
+  // 2k + half at position (2k + half) ^ swz(col).  V operand (O^T += V^T
+  // P^T) through transposed reads: in each 16-lane group g, source lane s
+  // points at key 16kk + 8r + 4(g >> 1) + s/4, dims 32dt + 16(g & 1) + 4(s & 3)
+  // .. +3; the read hands lane i of the group the 4 keys of dim
+  // 32dt + 16(g & 1) + i, matching the key order of P in S^T's registers.
+  const int g = lane >> 4, sl = lane & 15;
+  int v_row[2];
+  int v_byte[2][4];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    v_row[rr] = 8 * rr + 4 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int d = 32 * dt + 16 * (g & 1) + 4 * (sl & 3);
+      v_byte[rr][dt] = v_row[rr] * kRowBytes + (((d >> 3) ^ swz(v_row[rr])) << 4) + (d & 7) * 2;
+    }
+  }
 
-  // Per step each thread moves 4 K chunks (token tid/16 of each of the 4
-  // blocks) and 4 V chunks (tokens 4*(tid/16 % 4) + j of block tid/64).
-  uint4 kreg[4], vreg[4];
-  const int ktok = tid >> 4, dchunk = tid & 15;
-  const int kq = tid >> 4;  // key quad of the step for V: keys 4kq .. 4kq+3
-  auto load_step = [&](int kb) {
-    const int jb = kb / kBlockSize;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = jb + i;
-      const int id = j < nb ? row_table[j] : -1;
-      const bool ok = (unsigned)id < (unsigned)a.num_blocks && kb + 16 * i + ktok < L;
-      kreg[i] = ok ? *reinterpret_cast<const uint4*>(k_head + (size_t)id * block_stride + ktok * kHeadDim + dchunk * 8)
-                   : make_uint4(0u, 0u, 0u, 0u);
-    }
-    const int j = jb + (kq >> 2);
-    const int id = j < nb ? row_table[j] : -1;
-    const bool vid_ok = (unsigned)id < (unsigned)a.num_blocks;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = 4 * (kq & 3) + t;
-      const bool ok = vid_ok && kb + 4 * kq + t < L;
-      vreg[t] = ok ? *reinterpret_cast<const uint4*>(v_head + (size_t)id * block_stride + tok * kHeadDim + dchunk * 8)
-                   : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_step = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(lds + (16 * i + ktok) * kKRow + dchunk * 16) = kreg[i];
-    // keys 4kq..4kq+3 sit in group kq/4 at positions 4 * swap(kq % 4) .. +3
-    const int qi = kq & 3;
-    const int pos = 16 * (kq >> 2) + 4 * (((qi & 1) << 1) | (qi >> 1));
-    char* vt = lds + kKBytes;
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      uint2 pair;
-      pair.x = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
-      pair.y = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel);
-      *reinterpret_cast<uint2*>(vt + vt_offset(dchunk * 8 + e, pos)) = pair;
-    }
-  };
-  auto compute_step = [&](int kb) {
+  auto compute = [&](const char* st, int kb) {
+    const char* kt = st;
+    const char* vt = st + kTileBytes;
     float16_t s[2];
+    const float16_t zero = {};
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
+    for (int k = 0; k < 8; ++k) {  // the two key tiles' chains interleave
+      const int pos = (2 * k + half) ^ swz(col);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[T][i] = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const h8 ka = *reinterpret_cast<const h8*>(lds + (32 * T + col) * kKRow + (16 * k + 8 * half) * 2);
-        s[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[k], s[T], 0, 0, 0);
+      for (int T = 0; T < 2; ++T) {
+        const h8 ka = *reinterpret_cast<const h8*>(kt + (32 * T + col) * kRowBytes + pos * 16);
+        s[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[k], k == 0 ? zero : s[T], 0, 0, 0);
       }
     }
     // S^T[key = kb + 32T + 8(i/4) + 4*half + i%4][query col].  Keys past a
@@ -254,34 +377,63 @@ __device__ void prefill_tile(const PrefillArgs& a, int r, int qtile, int h, int 
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
       m = mn;
     }
-    float psum = 0.0f;
     h8 pb[4];
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[T][i], a.qk_scale, -m));
-        psum += p;
-        pb[2 * T + (i >> 3)][i & 7] = (_Float16)p;
+      for (int i = 0; i < 16; ++i) pb[2 * T + (i >> 3)][i & 7] = (_Float16)fast_exp2(fmaf(s[T][i], a.qk_scale, -m));
+    // the row sum of the FP16 weights the PV product uses, accumulated in fp32
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const half2_t pair = {pb[kk][e], pb[kk][e + 1]};
+        lsum = __builtin_amdgcn_fdot2(pair, ones, lsum, false);
       }
-    lsum += psum;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 va = *reinterpret_cast<const h8*>(lds + kKBytes + vt_offset(32 * dt + col, 16 * kk + 8 * half));
+      for (int dt = 0; dt < 4; ++dt) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS v4i16*)(vt + kk * kBlockSize * kRowBytes + v_byte[0][dt]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS v4i16*)(vt + kk * kBlockSize * kRowBytes + v_byte[1][dt]));
+        const h8 va = bitcast<h8>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kk], o[dt], 0, 0, 0);
       }
   };
 
-  load_step(k_begin);
-  for (int kb = k_begin; kb < k_end; kb += kBK) {
-    __syncthreads();  // the previous step's LDS reads are done
-    store_step();
-    __syncthreads();
-    const bool more = kb + kBK < k_end;
-    if (more) load_step(kb + kBK);  // next step's global loads fly during the MFMAs
-    if (kb <= p_wave_last) compute_step(kb);
+  __syncthreads();  // zero fill done before any direct load lands
+  const int nsteps = (k_end - k_begin + kBK - 1) / kBK;
+  // Step i lives in stage i % kStages.  At step i the loads of the next
+  // kStages - 2 steps may still fly; once every wave has passed the barrier,
+  // stage (i - 1) % kStages, last read at step i - 1, is refilled with step
+  // i + kStages - 1.
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u)
+    if (u < nsteps) {
+      if (u == 0) issue_step<0>(c, k_begin, 0);
+      if (u == 1) issue_step<1 % kStages>(c, k_begin + kBK, 1);
+      if (u == 2) issue_step<2 % kStages>(c, k_begin + 2 * kBK, 2);
+    }
+  auto run_step = [&](auto stage_tag, int i) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int kb = k_begin + i * kBK;
+    stage_wait(min(nsteps - 1 - i, kStages - 2));
+    if (i + kStages - 1 < nsteps) issue_step<(S + kStages - 1) % kStages>(c, kb + (kStages - 1) * kBK, i + kStages - 1);
+    if (kb <= p_wave_last) compute(prefill_stage<S>(), kb);
+  };
+  for (int i = 0; i < nsteps; i += kStages) {
+    run_step(std::integral_constant<int, 0>(), i);
+    if (i + 1 >= nsteps) break;
+    run_step(std::integral_constant<int, 1>(), i + 1);
+#if PKV_PREFILL_STAGES == 4
+    if (i + 2 >= nsteps) break;
+    run_step(std::integral_constant<int, 2>(), i + 2);
+    if (i + 3 >= nsteps) break;
+    run_step(std::integral_constant<int, 3>(), i + 3);
+#endif
   }
 
   lsum += shfl_xor(lsum, 32);
@@ -295,11 +447,11 @@ __device__ void prefill_tile(const PrefillArgs& a, int r, int qtile, int h, int 
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * half;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * dt + 8 * gq + 4 * half;
         uint2 w;
-        w.x = pack_half2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
-        w.y = pack_half2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+        w.x = pack_half2(o[dt][4 * gq] * inv, o[dt][4 * gq + 1] * inv);
+        w.y = pack_half2(o[dt][4 * gq + 2] * inv, o[dt][4 * gq + 3] * inv);
         *reinterpret_cast<uint2*>(orow + d0) = w;
       }
   } else {
@@ -308,24 +460,36 @@ __device__ void prefill_tile(const PrefillArgs& a, int r, int qtile, int h, int 
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * half;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * dt + 8 * gq + 4 * half;
         *reinterpret_cast<float4*>(po + d0) =
-            make_float4(o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]);
+            make_float4(o[dt][4 * gq], o[dt][4 * gq + 1], o[dt][4 * gq + 2], o[dt][4 * gq + 3]);
       }
     if (half == 0) a.part_ml[slot] = make_float2(m, lsum);
   }
 }
 
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  // Workgroup n runs on XCD n % 8.  Along each XCD's sequence the prefill
+  // tiles are spread evenly among the decode workgroups, so that a CU holds a
+  // matrix-core-bound tile and a memory-bound decode group at the same time.
+  // The prefill tiles an XCD gets are consecutive in (head, key range, query
+  // tile) order, so the tiles that re-read one (head, key range) share its L2.
   const int n = blockIdx.x;
-  if (n < a.prefill_wgs) {
-    // XCD-aware order: consecutive logical indices run on one XCD, and the
-    // innermost logical factor is the query tile, so the tiles that re-read
-    // the same (head, key range) share that XCD's L2.
-    const int per_xcd = a.prefill_wgs / kXcds;
-    const int logical = (n % kXcds) * per_xcd + n / kXcds;
+  const int x = n % kXcds;
+  const int m = n / kXcds;
+  const int np = a.prefill_wgs / kXcds;
+  const int nd = a.decode_wgs / kXcds;
+  const int tot = np + nd;
+#if PKV_PREFILL_INTERLEAVE
+  const int before = (int)((long long)m * np / tot);     // prefill positions before m
+  const int upto = (int)((long long)(m + 1) * np / tot);
+#else
+  const int before = m < np ? m : np;  // all of an XCD's prefill tiles first
+  const int upto = m < np ? m + 1 : np;
+#endif
+  if (upto > before) {
+    const int logical = x * np + before;
     const int tile = logical % a.tiles_max;
     const int rest = logical / a.tiles_max;
     const int kr = rest % a.ranges_max;
@@ -333,18 +497,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
     if (h >= a.num_heads) return;
     int row, qtile;
     if (!find_tile(a, tile, row, qtile)) return;
-    prefill_tile(a, row, qtile, h, kr, lds);
+    prefill_tile(a, row, qtile, h, kr);
     return;
   }
-  // decode rows: (row, 256-token range, group of 4 heads)
+  // decode rows: (row, 256-token range, group of kPrefillWaves heads)
   const int head_groups = (a.num_heads + kPrefillWaves - 1) / kPrefillWaves;
-  const int d = n - a.prefill_wgs;
+  const int d = (m - before) * kXcds + x;
   const int hg = d % head_groups;
   const int rs = d / head_groups;
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
-  const int h = hg * kPrefillWaves + (threadIdx.x >> 6);
+  const int h = __builtin_amdgcn_readfirstlane(hg * kPrefillWaves + (threadIdx.x >> 6));
   if (h >= a.num_heads) return;
   const int t = a.query_start[r];
   if (a.query_start[r + 1] - t != 1 || t < 0 || t >= a.total_q) return;
@@ -364,16 +528,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
 }
 
 // One wave per (query token, head): find the token's row, count its ranges,
-// merge when there is more than one.
+// merge when there is more than one.  query_start is non-decreasing.
 __global__ __launch_bounds__(kPrefillThreads) void prefill_merge_kernel(PrefillArgs a) {
   const int t = blockIdx.x;
-  const int h = blockIdx.y * kPrefillWaves + (threadIdx.x >> 6);
+  const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kPrefillWaves + (threadIdx.x >> 6));
   if (h >= a.num_heads) return;
-  int lo = 0, hi = a.num_rows - 1;  // last row with query_start[row] <= t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.query_start[mid] <= t) lo = mid; else hi = mid - 1;
+  // the token's row is the last one with query_start[row] <= t: count those
+  // rows with one parallel load per 64 rows instead of a dependent search
+  const int lane = threadIdx.x & 63;
+  int below = 0;
+  for (int r0 = 0; r0 < a.num_rows; r0 += 64) {
+    const int rr = r0 + lane;
+    below += __popcll(__ballot(rr < a.num_rows && a.query_start[rr] <= t));
   }
+  const int lo = below > 0 ? below - 1 : 0;
   const int r = lo;
   const int qs0 = a.query_start[r];
   const int n = a.query_start[r + 1] - qs0;
@@ -465,11 +633,13 @@ extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t lay
   int64_t pre = tiles * ranges * cache->num_heads;
   pre = (pre + kXcds - 1) / kXcds * kXcds;
   const int head_groups = (cache->num_heads + kPrefillWaves - 1) / kPrefillWaves;
-  const int64_t dec = (int64_t)num_rows * decode_splits(max_context_len) * head_groups;
+  int64_t dec = (int64_t)num_rows * decode_splits(max_context_len) * head_groups;
+  dec = (dec + kXcds - 1) / kXcds * kXcds;
   if (pre + dec > INT32_MAX || tiles > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
   a.tiles_max = (int)(tiles > 0 ? tiles : 1);
   a.ranges_max = (int)ranges;
   a.prefill_wgs = (int)pre;
+  a.decode_wgs = (int)dec;
   hipStream_t s = static_cast<hipStream_t>(stream);
   prefill_mixed_kernel<<<dim3((unsigned)(pre + dec)), dim3(kPrefillThreads), 0, s>>>(a);
   if (int rc = check_launch("prefill mixed kernel")) return rc;
