@@ -1,0 +1,180 @@
+"""Continuous-batching decode loop over the paged KV cache.
+
+Drives the hot path the way the serving loop on the pages does (LLM
+inference batching, faangrind, scheduler steps 4-7; Inference
+Infrastructure, seeitflow, "Why engines allocate in blocks"): every step
+  * rows that have generated their answer leave and release their blocks,
+  * waiting requests join; a prompt of at least `prefix_tokens` tokens shares
+    the ref-counted prefix blocks and its remaining prompt tokens are appended
+    into fresh private blocks ("fill"),
+  * each running row grows its table when its next token starts a block,
+    appends that token's K/V and runs decode attention over its context.
+All bookkeeping goes through the library's block pool and all device work
+through its kernels; this module only sequences the calls.
+
+Token K/V values and queries are seeded draws (torch's device generator):
+prompt tokens of request i from seed (seed, i), decode tokens and queries of
+step s from seed (seed, s).  The `log` keeps what a checker needs to
+rebuild any row's context independently.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from . import BLOCK_SIZE, BlockPool, PagedCache, append, decode_attention, decode_workspace_size
+
+
+def _seed(*parts: int) -> int:
+    h = 1469598103934665603
+    for p in parts:
+        h = ((h ^ (int(p) & 0xFFFFFFFF)) * 1099511628211) & 0xFFFFFFFFFFFF
+    return h
+
+
+@dataclasses.dataclass
+class Row:
+    req: int
+    prompt: int          # prompt tokens
+    answer: int          # tokens to generate
+    generated: int       # tokens generated so far
+    shared: int          # leading tokens held in the shared prefix blocks
+    table: np.ndarray    # int32 block ids (capacity = stride)
+    nblk: int            # entries of `table` in use
+
+    @property
+    def length(self) -> int:  # tokens cached before this step's new token
+        return self.prompt + self.generated
+
+
+class ContinuousBatchTrace:
+    def __init__(self, torch, *, seed=3, num_blocks=36864, max_rows=64, prefix_tokens=2000,
+                 prompt_range=(50, 8000), answer_range=(1, 1000), heads=32, stride=None, scale=None,
+                 device="cuda"):
+        self.torch = torch
+        self.seed = seed
+        self.H = heads
+        self.max_rows = max_rows
+        self.prefix_tokens = prefix_tokens - prefix_tokens % BLOCK_SIZE
+        self.prompt_range = prompt_range
+        self.answer_range = answer_range
+        self.dev = torch.device(device)
+        max_ctx = prompt_range[1] + answer_range[1]
+        self.stride = stride or -(-max_ctx // BLOCK_SIZE)
+        self.scale = scale if scale is not None else 1.0 / np.sqrt(128.0)
+        self.pool_d = torch.empty((num_blocks, 1, 2, heads, BLOCK_SIZE, 128), dtype=torch.float16, device=self.dev)
+        gen = torch.Generator(device=self.dev)
+        gen.manual_seed(_seed(seed, 0xF111))
+        self.pool_d.normal_(0.0, 1.0, generator=gen)
+        self.cache = PagedCache(self.pool_d)
+        rng = np.random.default_rng(seed)
+        self.pool = BlockPool(num_blocks, rng.permutation(num_blocks).astype(np.int32))
+        self.queue_rng = np.random.default_rng(_seed(seed, 0xA11))
+        self.next_req = 0
+        # the shared prefix: held once by the trace itself so it outlives its rows
+        self.prefix_ids = self.pool.alloc(self.prefix_tokens // BLOCK_SIZE)
+        self.rows: list[Row] = []
+        self.step_no = 0
+        self.max_ctx = max_ctx
+        ws = decode_workspace_size(self.cache, max_rows, max_ctx)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
+        self.log = {"prefix_ids": self.prefix_ids.copy(), "joins": [], "steps": []}
+
+    # ---------------------------------------------------------------- requests
+
+    def _draw_request(self):
+        p = int(self.queue_rng.integers(self.prompt_range[0], self.prompt_range[1] + 1))
+        a = int(self.queue_rng.integers(self.answer_range[0], self.answer_range[1] + 1))
+        req = self.next_req
+        self.next_req += 1
+        return req, p, a
+
+    def prompt_kv(self, req: int, first: int, last: int):
+        """Seeded K/V of prompt tokens first..last-1 of request `req`, [n, H, 128] each."""
+        torch = self.torch
+        gen = torch.Generator(device=self.dev)
+        gen.manual_seed(_seed(self.seed, 0xB0B, req))
+        n_all = last  # draw the whole prompt so any sub-range is reproducible
+        kv = torch.randn((2, n_all, self.H, 128), generator=gen, device=self.dev, dtype=torch.float16)
+        return kv[0, first:last].contiguous(), kv[1, first:last].contiguous()
+
+    def step_draws(self, step: int, n: int):
+        """Seeded new-token K/V and queries of a step, [n, H, 128] each."""
+        torch = self.torch
+        gen = torch.Generator(device=self.dev)
+        gen.manual_seed(_seed(self.seed, 0x57E9, step))
+        x = torch.randn((3, max(n, 1), self.H, 128), generator=gen, device=self.dev, dtype=torch.float16)
+        return x[0, :n].contiguous(), x[1, :n].contiguous(), x[2, :n].contiguous()
+
+    def _join(self, req, prompt, answer):
+        torch = self.torch
+        table = np.zeros(self.stride, dtype=np.int32)
+        shared = self.prefix_tokens if prompt >= self.prefix_tokens else 0
+        nblk = 0
+        if shared:
+            nshared = shared // BLOCK_SIZE
+            self.pool.ref(self.prefix_ids)
+            table[:nshared] = self.prefix_ids
+            nblk = nshared
+        nblk = self.pool.grow(table, nblk, prompt)
+        row = Row(req, prompt, answer, 0, shared, table, nblk)
+        # fill: the private prompt tokens' K/V go into the fresh blocks
+        if prompt > shared:
+            k, v = self.prompt_kv(req, shared, prompt)
+            pos = torch.arange(shared, prompt, dtype=torch.int32, device=self.dev)
+            rot = torch.zeros(prompt - shared, dtype=torch.int32, device=self.dev)
+            tab = torch.from_numpy(table[None, :].copy()).to(self.dev)
+            append(self.cache, 0, k, v, pos, rot, tab)
+        self.log["joins"].append((req, prompt, answer, shared, self.step_no))
+        return row
+
+    def _leave(self, row: Row):
+        self.pool.free(row.table[:row.nblk])
+
+    # ---------------------------------------------------------------- one step
+
+    def step(self, events=None):
+        """Leave, join, grow, append one token per row, decode.  Returns the
+        step's row snapshot (for checkers) and, with events=(start, mid, end),
+        records them around the fill and the decode part."""
+        torch = self.torch
+        finished = [r for r in self.rows if r.generated >= r.answer]
+        for r in finished:
+            self._leave(r)
+        self.rows = [r for r in self.rows if r.generated < r.answer]
+        if events:
+            events[0].record()
+        while len(self.rows) < self.max_rows:
+            self.rows.append(self._join(*self._draw_request()))
+        if events:
+            events[1].record()
+        R = len(self.rows)
+        for r in self.rows:  # the new token sits at position r.length
+            r.nblk = self.pool.grow(r.table, r.nblk, r.length + 1)
+        tables = np.stack([r.table for r in self.rows])
+        lens = np.array([r.length + 1 for r in self.rows], dtype=np.int32)
+        k, v, q = self.step_draws(self.step_no, R)
+        tab_d = torch.from_numpy(tables).to(self.dev)
+        pos_d = torch.from_numpy(lens - 1).to(self.dev)
+        rot_d = torch.arange(R, dtype=torch.int32, device=self.dev)
+        lens_d = torch.from_numpy(lens).to(self.dev)
+        out = torch.empty((R, self.H, 128), dtype=torch.float16, device=self.dev)
+        append(self.cache, 0, k, v, pos_d, rot_d, tab_d)
+        decode_attention(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, self.ws)
+        if events:
+            events[2].record()
+        snap = {"step": self.step_no, "reqs": [r.req for r in self.rows], "lens": lens.copy(),
+                "gen_index": [r.generated for r in self.rows], "tables": tables.copy(), "out": out}
+        self.log["steps"].append({"step": self.step_no, "reqs": snap["reqs"], "lens": lens.copy(),
+                                  "new_pos": (lens - 1).copy()})
+        for r in self.rows:
+            r.generated += 1
+        self.step_no += 1
+        return snap
+
+    def drain(self):
+        for r in self.rows:
+            self._leave(r)
+        self.rows = []
+        self.pool.free(self.prefix_ids)
