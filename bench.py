@@ -134,6 +134,47 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
     }
 
 
+def measure_trace(torch, steps=300, warm=5):
+    """Continuous-batching trace: up to 64 rows over a 36,864-block one-layer
+    pool, prompts U{50..8000}, answers U{1..1000}, a 2,000-token prefix
+    shared by reference counts; rows leave and are refilled every step.
+    The decode part of a step (grow, append one token per row, decode) is
+    timed with events separately from the fill of joining rows."""
+    from paged_kv_cache_pkv_amd.trace import ContinuousBatchTrace
+
+    tr = ContinuousBatchTrace(torch, seed=3, num_blocks=36864, max_rows=64, prefix_tokens=2000,
+                              prompt_range=(50, 8000), answer_range=(1, 1000))
+    for _ in range(warm):
+        tr.step()
+    torch.cuda.synchronize()
+    rec = []
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        snap = tr.step(events=ev)
+        rec.append((ev, int(snap["lens"].sum()), len(snap["reqs"])))
+    torch.cuda.synchronize()
+    fill_ms = np.array([e[0].elapsed_time(e[1]) for e, _, _ in rec])
+    step_ms = np.array([e[1].elapsed_time(e[2]) for e, _, _ in rec])
+    tokens = np.array([t for _, t, _ in rec], dtype=np.float64)
+    joins = sum(1 for j in tr.log["joins"] if j[4] >= warm)
+    tr.drain()
+    assert tr.pool.num_free == 36864, "trace leaked blocks"
+    return {
+        "workload": "continuous-batching trace: <=64 rows, one layer 32x128 FP16, 36,864-block pool, "
+                    "prompts U{50..8000}, answers U{1..1000}, 2,000-token prefix shared by 125 ref-counted blocks",
+        "steps": steps,
+        "decode_step_ms_p50": float(np.percentile(step_ms, 50)),
+        "decode_step_ms_p90": float(np.percentile(step_ms, 90)),
+        "decode_step_ms_max": float(step_ms.max()),
+        "logical_kv_tokens_per_step_mean": float(tokens.mean()),
+        "kv_tokens_per_s": float(tokens.sum() / (step_ms.sum() / 1e3)),
+        "logical_tb_s": float(tokens.sum() * LAYER_TOKEN_BYTES / (step_ms.sum() / 1e3) / 1e12),
+        "joins": joins,
+        "fill_ms_total": float(fill_ms.sum()),
+        "pool_drained": True,
+    }
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +185,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-trace", action="store_true", help="skip the continuous-batching trace")
+    ap.add_argument("--trace-steps", type=int, default=300)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a known-size kernel for "
                          "calibrating HBM byte counters)")
@@ -342,6 +385,10 @@ def main():
     if not args.no_prefill:
         prefill = measure_prefill(torch, pkv, dev, stream)
 
+    trace = None
+    if not args.no_trace:
+        trace = measure_trace(torch, steps=args.trace_steps)
+
     rec = {
         "metric": METRIC,
         "value": value,
@@ -370,6 +417,7 @@ def main():
         "wall_s_timed": wall,
         "parity_step0_layer0": parity,
         "prefill": prefill,
+        "trace": trace,
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(rec), flush=True)
