@@ -218,6 +218,18 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o,
     const float w_mine = fast_exp2(mine.x - M);
     const int n = min(64, nsplit - s0);
     int j = 0;
+    // up to 16 independent partial loads in flight per lane
+    for (; j + 16 <= n; j += 16) {
+      float2 p[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) p[u] = po[(size_t)(s0 + j + u) * (kHeadDim / 2)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), j + u));
+        o0 = fmaf(p[u].x, w, o0);
+        o1 = fmaf(p[u].y, w, o1);
+      }
+    }
     for (; j + 4 <= n; j += 4) {
       float2 p[4];
 #pragma unroll

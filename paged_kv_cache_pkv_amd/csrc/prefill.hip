@@ -9,13 +9,14 @@
 // request (LLM inference batching, faangrind, "Prefill and decode share each
 // step"), so one launch serves both.
 //
-// Prefill tiles (rows with n >= 2).  A workgroup of 8 waves owns 256 queries
+// Prefill tiles (rows with n >= 2).  A workgroup of 4 waves owns 128 queries
 // of one head and one fixed range of kPrefillSplit keys; wave w owns 32
 // queries.  Keys advance 64 at a time: four 16-token blocks gathered through
-// the block table by direct global->LDS loads (no registers), four LDS stages
-// deep so the loads run three steps ahead of the matrix cores.  K and V sit in
-// LDS row-major; V reaches the MFMA transposed through ds_read_b64_tr_b16.  On
-// v_mfma_f32_32x32x16_f16:
+// the block table by direct global->LDS loads (no registers), with K one step
+// further ahead than V, so that each wave starts the next step's QK^T on the
+// matrix cores before it computes this step's softmax on the vector ALUs.  K
+// and V sit in LDS row-major; V reaches the MFMA transposed through
+// ds_read_b64_tr_b16.  On v_mfma_f32_32x32x16_f16:
 //   S^T = K Q^T      A = K rows from LDS, B = the wave's queries (registers)
 //   O^T += V^T P^T   A = V^T via transposed LDS reads, B = P straight from
 //                    S^T's registers
@@ -37,13 +38,7 @@
 namespace pkv {
 namespace {
 
-#ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 4
-#endif
-#ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 2
-#endif
-constexpr int kPrefillThreads = 64 * PKV_PREFILL_WAVES;
+constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kQPerWave = 32;
 constexpr int kBQ = kPrefillWaves * kQPerWave;  // queries per tile
@@ -59,36 +54,31 @@ static_assert(kPrefillSplit % kBK == 0, "ranges hold whole key steps");
 static_assert(kPrefillSplit / kBK <= 64, "a range's block ids for one slot fit one wave");
 constexpr int kRowBytes = kHeadDim * 2;        // one key's 128 dims
 constexpr int kTileBytes = kBK * kRowBytes;     // K (or V) of one step: 16 KiB
-constexpr int kStageBytes = 2 * kTileBytes;     // K tile then V tile
 constexpr int kXcds = 8;
-constexpr int kStages = PKV_PREFILL_STAGES;  // LDS stages: direct loads run kStages - 1 steps ahead
-static_assert(kStages == 2 || kStages == 4, "2 or 4 LDS stages");
-static_assert(kPrefillWaves == 4 || kPrefillWaves == 8, "4 or 8 waves per tile");
-// direct loads each wave issues per step: with 4 waves a wave gathers one
-// block's K and V (8 loads), with 8 waves one block's K or V (4 loads)
-constexpr int kLoadsPerStep = kPrefillWaves == 4 ? 8 : 4;
+static_assert(kPrefillWaves == 4, "one wave per block of a step");
 
-// Two LDS stages, as distinct objects so that the compiler can tell the stage
-// being filled by direct loads from the stage being read.  Rows are 256 bytes
-// (16 chunks of 16 bytes, no padding); chunk c of tile row r is stored at
-// position c ^ swz(r), swz swapping the two 2-bit halves of r & 15.  Then the
-// 16 consecutive rows of one K operand read land on 16 distinct positions, and
-// so do the 4 rows x 4 chunks of one transposed V read: both are free of bank
-// conflicts.
-__shared__ __attribute__((aligned(16))) char g_prefill_stage0[kStageBytes];
-__shared__ __attribute__((aligned(16))) char g_prefill_stage1[kStageBytes];
-#if PKV_PREFILL_STAGES == 4
-__shared__ __attribute__((aligned(16))) char g_prefill_stage2[kStageBytes];
-__shared__ __attribute__((aligned(16))) char g_prefill_stage3[kStageBytes];
-#endif
+// LDS: three K tiles and two V tiles (80 KiB), as distinct objects so that
+// the compiler can tell a tile being filled by direct loads from one being
+// read.  Step i's keys sit in K tile i % 3 and its values in V tile i % 2:
+// while step i's softmax and P*V run, the QK^T of step i+1 already reads its
+// K tile.  Rows are 256 bytes (16 chunks of 16 bytes, no padding); chunk c of
+// tile row r is stored at position c ^ swz(r), swz swapping the two 2-bit
+// halves of r & 15.  Then the 16 consecutive rows of one K operand read land
+// on 16 distinct positions, and so do the 4 rows x 4 chunks of one
+// transposed V read: both are free of bank conflicts.
+__shared__ __attribute__((aligned(16))) char g_k_tile0[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_k_tile1[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_k_tile2[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_v_tile0[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_v_tile1[kTileBytes];
 
 template <int S>
-__device__ __forceinline__ char* prefill_stage() {
-#if PKV_PREFILL_STAGES == 4
-  return S == 0 ? g_prefill_stage0 : S == 1 ? g_prefill_stage1 : S == 2 ? g_prefill_stage2 : g_prefill_stage3;
-#else
-  return S == 0 ? g_prefill_stage0 : g_prefill_stage1;
-#endif
+__device__ __forceinline__ char* k_tile() {
+  return S == 0 ? g_k_tile0 : S == 1 ? g_k_tile1 : g_k_tile2;
+}
+template <int S>
+__device__ __forceinline__ char* v_tile() {
+  return S == 0 ? g_v_tile0 : g_v_tile1;
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -154,15 +144,6 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ h8 as_h8(const uint4& v) { return bitcast<h8>(v); }
 
-// Wait for this wave's outstanding direct loads, then a workgroup barrier;
-// the empty asm statements keep the compiler from moving memory accesses
-// across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 template <typename T>
@@ -182,15 +163,14 @@ struct TileCtx {
   int voff[4];              // this lane's source byte offsets for the 4 row quads of a block
 };
 
-// Each step gathers four 16-token blocks (kb / 16 + b, b = 0..3).  With 4
-// waves, wave b loads block b's K rows and then its V rows; with 8 waves,
-// waves 0-3 load the K rows and waves 4-7 the V rows.  Every load is a direct
-// 1 KiB global->LDS transfer in which each lane fetches the chunk that the
+// Each step gathers four 16-token blocks (kb / 16 + w, w = 0..3): wave w
+// loads block w's K rows into a K tile or its V rows into a V tile, 4 direct
+// 1 KiB global->LDS transfers in which each lane fetches the chunk that the
 // swizzle puts in its LDS slot.  The buffer resource covers only the block's
 // live rows, so rows past the context (and whole blocks with an invalid id)
 // read as zero.
-template <int S>
-__device__ __forceinline__ void issue_half(const TileCtx& c, int kb, int step, int blk, bool is_v) {
+__device__ __forceinline__ void issue_rows(const TileCtx& c, char* tile, int kb, int step, bool is_v) {
+  const int blk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int first = kb + kBlockSize * blk;
   int rows = c.L - first;
   rows = rows < 0 ? 0 : (rows > kBlockSize ? kBlockSize : rows);
@@ -201,35 +181,16 @@ __device__ __forceinline__ void issue_half(const TileCtx& c, int kb, int step, i
       uniform_ptr(c.k_head + (ok ? (size_t)id * c.block_stride : 0) + (is_v ? c.vdelta : 0));
   const int nrec = __builtin_amdgcn_readfirstlane(ok ? rows * kRowBytes : 0);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, nrec, 0x00020000);
-  char* dst = prefill_stage<S>() + (is_v ? kTileBytes : 0) + kBlockSize * blk * kRowBytes;
+  char* dst = tile + kBlockSize * blk * kRowBytes;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PKV_LDS void*)(dst + 4 * q * kRowBytes), 16, c.voff[q], 0, 0, 0);
 }
 
-template <int S>
-__device__ __forceinline__ void issue_step(const TileCtx& c, int kb, int step) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (kPrefillWaves == 4) {
-    issue_half<S>(c, kb, step, wave, false);
-    issue_half<S>(c, kb, step, wave, true);
-  } else {
-    issue_half<S>(c, kb, step, wave & 3, wave >= 4);
-  }
-}
-
-// Wait until at most `ahead` later steps' loads are outstanding for this wave,
-// then synchronise the workgroup.
-__device__ __forceinline__ void stage_wait(int ahead) {
-  if (ahead >= 2) {
-    if (kLoadsPerStep == 8) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  } else if (ahead == 1) {
-    if (kLoadsPerStep == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+// All of this wave's direct loads have landed and its LDS reads have
+// returned; then the workgroup meets.
+__device__ __forceinline__ void loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -262,7 +223,6 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
   const bool q_ok = wq < q_end;
   const int p_q = q_ok ? L - n + wq : -1;
   const int wq0 = q_begin + wave * kQPerWave;  // the wave's first query
-  const int p_wave_last = wq0 < q_end ? L - n + min(q_end, wq0 + kQPerWave) - 1 : -1;
   const int p_wave_first = L - n + wq0;
 
   TileCtx c;
@@ -270,7 +230,7 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
     // one load brings every step's block id for this wave's block slot
     const int32_t* row_table = a.block_tables + (size_t)r * a.bt_stride;
     const int nb = (L + kBlockSize - 1) / kBlockSize;
-    const int j = k_begin / kBlockSize + 4 * lane + (kPrefillWaves == 4 ? wave : (wave & 3));
+    const int j = k_begin / kBlockSize + 4 * lane + wave;
     c.ids = (lane < kPrefillSplit / kBK && j < nb) ? row_table[j] : -1;
   }
   c.block_stride = (size_t)a.num_layers * 2 * a.num_heads * kBlockSize * kHeadDim;
@@ -289,13 +249,12 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
   // Stale LDS from earlier workgroups must never meet a zero weight as NaN.
   {
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    for (int i = tid; i < kStageBytes / 16; i += kPrefillThreads) {
-      reinterpret_cast<uint4*>(g_prefill_stage0)[i] = z;
-      reinterpret_cast<uint4*>(g_prefill_stage1)[i] = z;
-#if PKV_PREFILL_STAGES == 4
-      reinterpret_cast<uint4*>(g_prefill_stage2)[i] = z;
-      reinterpret_cast<uint4*>(g_prefill_stage3)[i] = z;
-#endif
+    for (int i = tid; i < kTileBytes / 16; i += kPrefillThreads) {
+      reinterpret_cast<uint4*>(g_k_tile0)[i] = z;
+      reinterpret_cast<uint4*>(g_k_tile1)[i] = z;
+      reinterpret_cast<uint4*>(g_k_tile2)[i] = z;
+      reinterpret_cast<uint4*>(g_v_tile0)[i] = z;
+      reinterpret_cast<uint4*>(g_v_tile1)[i] = z;
     }
   }
 
@@ -336,107 +295,156 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
     }
   }
 
-  auto compute = [&](const char* st, int kb) {
-    const char* kt = st;
-    const char* vt = st + kTileBytes;
-    float16_t s[2];
-    const float16_t zero = {};
+  // The work runs in half steps of 32 keys (rows 32T .. 32T+31 of a tile).
+  // Scores of a half step in S^T's accumulator layout: register i of lane
+  // (col, half) holds key 32T + 8(i/4) + 4*half + i%4 of query col.
+  const float16_t zero = {};
+  // S^T = K Q^T for one half step from a K tile.
+  auto qk = [&](const char* kt, int T, float16_t& sc) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {  // the two key tiles' chains interleave
+    for (int k = 0; k < 8; ++k) {
       const int pos = (2 * k + half) ^ swz(col);
+      const h8 ka = *reinterpret_cast<const h8*>(kt + (32 * T + col) * kRowBytes + pos * 16);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[k], k == 0 ? zero : sc, 0, 0, 0);
+    }
+  };
+  // Keys after the query's position get -inf; kb is the half step's first key.
+  auto mask = [&](float16_t& sc, int kb) {
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        const h8 ka = *reinterpret_cast<const h8*>(kt + (32 * T + col) * kRowBytes + pos * 16);
-        s[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[k], k == 0 ? zero : s[T], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+      if (key > p_q) sc[i] = -INFINITY;
+    }
+  };
+  // The half step's largest scaled score of this lane's query (both lane halves).
+  auto step_max = [&](const float16_t& sc) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x = fmaxf(x, sc[i]);
+    const auto both = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(both[0]), __uint_as_float(both[1])) * a.qk_scale;
+  };
+  // Weights 2^(s * scale - m) rounded to FP16 as the P*V operand, and their
+  // row sum (of the FP16 values the product uses) accumulated in fp32.
+  auto weights = [&](const float16_t& sc, h8* pb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pb[i >> 3][i & 7] = (_Float16)fast_exp2(fmaf(sc[i], a.qk_scale, -m));
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float ls = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const half2_t pair = {pb[kk][e], pb[kk][e + 1]};
+        ls = __builtin_amdgcn_fdot2(pair, ones, ls, false);
       }
+    return ls;
+  };
+  // O^T += V^T P^T for one half step from a V tile: blocks 2T and 2T + 1.
+  auto pv = [&](const h8* pb, const char* vt, int T) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const char* vb = vt + (2 * T + kk) * kBlockSize * kRowBytes;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS v4i16*)(vb + v_byte[0][dt]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS v4i16*)(vb + v_byte[1][dt]));
+        const h8 va = bitcast<h8>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kk], o[dt], 0, 0, 0);
+      }
+  };
+  // One half step: the QK^T of the next half step (into s_next) on the
+  // matrix cores while this half step's softmax (of s_cur) runs on the
+  // vector ALUs -- no branch in between, so the two interleave -- then this
+  // half step's P*V.
+  //
+  // The exponent reference m moves only when a score exceeds it by more
+  // than kLazy (log2 units).  Weights then stay below 2^kLazy, well inside
+  // FP16, and the common half step computes its weights without waiting for
+  // its own maximum.  O and the row sum are relative to the same m, so the
+  // result is the same softmax; partial ranges carry m to the merge.
+  constexpr float kLazy = 8.0f;
+  auto half_step = [&](const char* kt_next, int t_next, float16_t& s_next, float16_t& s_cur, const char* vt, int t_cur) {
+    qk(kt_next, t_next, s_next);
+    const float mstep = step_max(s_cur);
+    h8 pb[2];
+    float ls = weights(s_cur, pb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // two transcendental
     }
-    // S^T[key = kb + 32T + 8(i/4) + 4*half + i%4][query col].  Keys past a
-    // query's position only occur on the diagonal steps.
-    if (kb + kBK - 1 > p_wave_first) {
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + 32 * T + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key > p_q) s[T][i] = -INFINITY;
-        }
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[T][i]);
-    mloc = fmaxf(mloc, shfl_xor(mloc, 32)) * a.qk_scale;  // scaled maximum of this step
-    const float mn = fmaxf(m, mloc);
-    if (__any(mn > m)) {  // the running maximum moved for some query: rescale
+    // Keep the common path's weights in this block: the rescale branch
+    // overwrites them, and without this the compiler would move their
+    // computation past the branch, away from the MFMAs it should overlap.
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(ls));
+    if (__any(mstep > m + kLazy)) {
+      const float mn = fmaxf(m, mstep);
       const float alpha = fast_exp2(m - mn);
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        for (int r2 = 0; r2 < 16; ++r2) o[dt][r2] *= alpha;
       m = mn;
+      ls = weights(s_cur, pb);
     }
-    h8 pb[4];
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pb[2 * T + (i >> 3)][i & 7] = (_Float16)fast_exp2(fmaf(s[T][i], a.qk_scale, -m));
-    // the row sum of the FP16 weights the PV product uses, accumulated in fp32
-    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const half2_t pair = {pb[kk][e], pb[kk][e + 1]};
-        lsum = __builtin_amdgcn_fdot2(pair, ones, lsum, false);
-      }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (PKV_LDS v4i16*)(vt + kk * kBlockSize * kRowBytes + v_byte[0][dt]));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (PKV_LDS v4i16*)(vt + kk * kBlockSize * kRowBytes + v_byte[1][dt]));
-        const h8 va = bitcast<h8>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kk], o[dt], 0, 0, 0);
-      }
+    lsum += ls;
+    pv(pb, vt, t_cur);
   };
 
   __syncthreads();  // zero fill done before any direct load lands
   const int nsteps = (k_end - k_begin + kBK - 1) / kBK;
-  // Step i lives in stage i % kStages.  At step i the loads of the next
-  // kStages - 2 steps may still fly; once every wave has passed the barrier,
-  // stage (i - 1) % kStages, last read at step i - 1, is refilled with step
-  // i + kStages - 1.
-#pragma unroll
-  for (int u = 0; u < kStages - 1; ++u)
-    if (u < nsteps) {
-      if (u == 0) issue_step<0>(c, k_begin, 0);
-      if (u == 1) issue_step<1 % kStages>(c, k_begin + kBK, 1);
-      if (u == 2) issue_step<2 % kStages>(c, k_begin + 2 * kBK, 2);
-    }
-  auto run_step = [&](auto stage_tag, int i) {
-    constexpr int S = decltype(stage_tag)::value;
+  // Step i (64 keys): K in tile i % 3, V in tile i % 2.  Iteration i waits
+  // for the loads issued one iteration earlier (K of step i+1, V of step i),
+  // then refills the tiles nobody reads any more (K of step i+2 into the
+  // tile of step i-1, V of step i+1 into the tile of step i-1), then runs
+  // its two half steps; the second one's QK^T is the first half of step i+1.
+  float16_t s0, s1;
+  issue_rows(c, k_tile<0>(), k_begin, 0, false);
+  issue_rows(c, v_tile<0>(), k_begin, 0, true);
+  if (nsteps > 1) issue_rows(c, k_tile<1>(), k_begin + kBK, 1, false);
+  loads_barrier();
+  qk(k_tile<0>(), 0, s0);
+  if (k_begin + 31 > p_wave_first) mask(s0, k_begin);
+  auto iteration = [&](auto ktag, auto vtag, int i) {
+    constexpr int SK = decltype(ktag)::value;  // i % 3
+    constexpr int SV = decltype(vtag)::value;  // i % 2
     const int kb = k_begin + i * kBK;
-    stage_wait(min(nsteps - 1 - i, kStages - 2));
-    if (i + kStages - 1 < nsteps) issue_step<(S + kStages - 1) % kStages>(c, kb + (kStages - 1) * kBK, i + kStages - 1);
-    if (kb <= p_wave_last) compute(prefill_stage<S>(), kb);
+    loads_barrier();
+    if (i + 2 < nsteps) issue_rows(c, k_tile<(SK + 2) % 3>(), kb + 2 * kBK, i + 2, false);
+    if (i + 1 < nsteps) issue_rows(c, v_tile<(SV + 1) % 2>(), kb + kBK, i + 1, true);
+    half_step(k_tile<SK>(), 1, s1, s0, v_tile<SV>(), 0);
+    if (kb + 63 > p_wave_first) mask(s1, kb + 32);
+    // After the last step the next K tile holds an older step's keys (finite
+    // values or zeros); those scores are never used.
+    half_step(k_tile<(SK + 1) % 3>(), 0, s0, s1, v_tile<SV>(), 1);
+    if (kb + 95 > p_wave_first) mask(s0, kb + 64);
   };
-  for (int i = 0; i < nsteps; i += kStages) {
-    run_step(std::integral_constant<int, 0>(), i);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int i = 0; i < nsteps; i += 6) {
+    iteration(I0(), I0(), i);
     if (i + 1 >= nsteps) break;
-    run_step(std::integral_constant<int, 1>(), i + 1);
-#if PKV_PREFILL_STAGES == 4
+    iteration(I1(), I1(), i + 1);
     if (i + 2 >= nsteps) break;
-    run_step(std::integral_constant<int, 2>(), i + 2);
+    iteration(I2(), I0(), i + 2);
     if (i + 3 >= nsteps) break;
-    run_step(std::integral_constant<int, 3>(), i + 3);
-#endif
+    iteration(I0(), I1(), i + 3);
+    if (i + 4 >= nsteps) break;
+    iteration(I1(), I0(), i + 4);
+    if (i + 5 >= nsteps) break;
+    iteration(I2(), I1(), i + 5);
   }
 
-  lsum += shfl_xor(lsum, 32);
+  {
+    const auto both = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(both[0]) + __uint_as_float(both[1]);
+  }
   if (!q_ok) return;
   const int nsplit_q = p_q / kPrefillSplit + 1;
   if (kr >= nsplit_q) return;
