@@ -93,6 +93,7 @@ struct PrefillArgs {
   const int32_t* context_lens;
   float* part_o;               // [T][H][S][128]
   float2* part_ml;             // [T][H][S]
+  int32_t* tok_splits;         // [T] ranges each query token was cut into
   int layer, num_blocks, num_layers, num_heads;
   int bt_stride, num_rows, total_q, max_context_len, max_splits;
   int tiles_max, ranges_max;   // prefill grid factors
@@ -447,6 +448,7 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
   }
   if (!q_ok) return;
   const int nsplit_q = p_q / kPrefillSplit + 1;
+  if (kr == 0 && h == 0 && half == 0) a.tok_splits[qs0 + wq] = nsplit_q;
   if (kr >= nsplit_q) return;
   const size_t th = (size_t)(qs0 + wq) * a.num_heads + h;
   if (nsplit_q == 1) {
@@ -523,6 +525,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
   int L = a.context_lens[r];
   L = L > a.max_context_len ? a.max_context_len : L;
   const size_t th = (size_t)t * a.num_heads + h;
+  if (split == 0 && h == 0 && (threadIdx.x & 63) == 0) a.tok_splits[t] = L < 1 ? 1 : decode_splits(L);
   if (L < 1) {
     if (split == 0 && (threadIdx.x & 63) < 16)
       reinterpret_cast<uint4*>(a.out)[th * 16 + (threadIdx.x & 15)] = make_uint4(0u, 0u, 0u, 0u);
@@ -535,35 +538,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
                reinterpret_cast<uint4*>(a.out) + th * 16, a.part_o + slot * kHeadDim, a.part_ml + slot);
 }
 
-// One wave per (query token, head): find the token's row, count its ranges,
-// merge when there is more than one.  query_start is non-decreasing.
+// One wave per (query token, head): merge the token's ranges when there is
+// more than one.  The attention launch recorded each token's range count;
+// a token it did not reach (a row that breaks the call's contract) reads a
+// count clamped to the workspace, so its output is unspecified but every
+// access stays inside the workspace.
 __global__ __launch_bounds__(kPrefillThreads) void prefill_merge_kernel(PrefillArgs a) {
   const int t = blockIdx.x;
   const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kPrefillWaves + (threadIdx.x >> 6));
   if (h >= a.num_heads) return;
-  // the token's row is the last one with query_start[row] <= t: count those
-  // rows with one parallel load per 64 rows instead of a dependent search
-  const int lane = threadIdx.x & 63;
-  int below = 0;
-  for (int r0 = 0; r0 < a.num_rows; r0 += 64) {
-    const int rr = r0 + lane;
-    below += __popcll(__ballot(rr < a.num_rows && a.query_start[rr] <= t));
-  }
-  const int lo = below > 0 ? below - 1 : 0;
-  const int r = lo;
-  const int qs0 = a.query_start[r];
-  const int n = a.query_start[r + 1] - qs0;
-  if (t - qs0 >= n) return;
-  int L = a.context_lens[r];
-  L = L > a.max_context_len ? a.max_context_len : L;
-  if (L < 1 || L < n) return;
-  int nsplit;
-  if (n == 1) {
-    nsplit = decode_splits(L);
-  } else {
-    const int p = L - n + (t - qs0);
-    nsplit = p / kPrefillSplit + 1;
-  }
+  int nsplit = a.tok_splits[t];
+  nsplit = nsplit > a.max_splits ? a.max_splits : nsplit;
   if (nsplit <= 1) return;
   const size_t th = (size_t)t * a.num_heads + h;
   merge_partials(a.part_o + th * a.max_splits * kHeadDim, a.part_ml + th * a.max_splits, nsplit,
@@ -586,7 +571,7 @@ extern "C" size_t pkv_prefill_workspace_size(const pkv_cache* cache, int32_t num
   (void)max_q_per_row;
   if (!cache || total_q < 1 || max_context_len < 1 || cache->num_heads < 1) return 0;
   const size_t n = (size_t)total_q * cache->num_heads * prefill_max_splits(max_context_len);
-  return align256(n * kHeadDim * sizeof(float)) + align256(n * sizeof(float2));
+  return align256(n * kHeadDim * sizeof(float)) + align256(n * sizeof(float2)) + align256((size_t)total_q * sizeof(int32_t));
 }
 
 extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t layer, void* out, const void* q,
@@ -625,6 +610,8 @@ extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t lay
   const size_t n = (size_t)total_q * cache->num_heads * a.max_splits;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + align256(n * kHeadDim * sizeof(float)));
+  a.tok_splits = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(n * kHeadDim * sizeof(float)) +
+                                            align256(n * sizeof(float2)));
   a.layer = layer;
   a.num_blocks = cache->num_blocks;
   a.num_layers = cache->num_layers;
