@@ -186,11 +186,102 @@ def parse():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-trace", action="store_true", help="skip the continuous-batching trace")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-context step and the block copies")
     ap.add_argument("--trace-steps", type=int, default=300)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a known-size kernel for "
                          "calibrating HBM byte counters)")
     return ap.parse_args()
+
+
+def measure_block_copies(torch, pkv, cache, free_ids, stream, n=64, reps=10):
+    """Copy-on-write and swap of whole 8 MiB blocks (all 32 layers) among free
+    blocks of the decode pool: n pairs per copy launch, n blocks per swap."""
+    if len(free_ids) < 2 * n:
+        return None
+    dev = cache.pool.device
+    bb = pkv.block_bytes(cache)
+    src = torch.from_numpy(np.ascontiguousarray(free_ids[:n], dtype=np.int32)).to(dev)
+    dst = torch.from_numpy(np.ascontiguousarray(free_ids[n:2 * n], dtype=np.int32)).to(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    pkv.copy_blocks(cache, src, dst, stream=stream)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        pkv.copy_blocks(cache, src, dst, stream=stream)
+    ev[1].record(stream)
+    host = torch.empty(n * bb, dtype=torch.uint8, pin_memory=True)
+    out_ids, in_ids = free_ids[:n], free_ids[n:2 * n]
+    pkv.swap_out(cache, out_ids, host, stream=stream)
+    pkv.swap_in(cache, host, in_ids, stream=stream)
+    torch.cuda.synchronize()
+    ev[2].record(stream)
+    for _ in range(reps):
+        pkv.swap_out(cache, out_ids, host, stream=stream)
+    ev[3].record(stream)
+    for _ in range(reps):
+        pkv.swap_in(cache, host, in_ids, stream=stream)
+    ev[4].record(stream)
+    torch.cuda.synchronize()
+    copy_ms = ev[0].elapsed_time(ev[1]) / reps
+    out_ms = ev[2].elapsed_time(ev[3]) / reps
+    in_ms = ev[3].elapsed_time(ev[4]) / reps
+    moved = n * bb
+    copy_gbs = 2 * moved / (copy_ms / 1e3) / 1e9  # each byte read once and written once
+    return {
+        "workload": f"{n} whole blocks of {bb >> 20} MiB (32 layers x 32 heads) among free blocks of the decode pool",
+        "copy_on_write_us": copy_ms * 1e3,
+        "copy_roofline": {"bound": "hbm", "achieved": copy_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": copy_gbs / HBM_PEAK_GBS, "traffic": None,
+                          "kernel": "copy_blocks_kernel (read + write bytes)"},
+        "swap_out_gb_s": moved / (out_ms / 1e3) / 1e9,
+        "swap_in_gb_s": moved / (in_ms / 1e3) / 1e9,
+        "swap_note": "device <-> pinned host over the host link, one DMA copy per run of consecutive ids",
+    }
+
+
+def measure_long_context(torch, pkv, cache, stream, steps=5, warm=2):
+    """The 13 x 8,192-token long-context step (seed 2) on the 32-layer pool:
+    per layer, append the 13 new tokens and run decode attention."""
+    from workloads import SCALE, c3_long_context
+
+    b = c3_long_context(seed=2, with_pool=False)
+    dev = cache.pool.device
+    NL = int(cache.desc.num_layers)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    tables, lens, pos, rot = d(b.block_tables), d(b.context_lens), d(b.positions), d(b.request_of_token)
+    q, k, v = d(b.q[0]), d(b.k_new[0]), d(b.v_new[0])
+    maxL = int(b.context_lens.max())
+    ws = torch.empty(pkv.decode_workspace_size(cache, b.rows, maxL), dtype=torch.uint8, device=dev)
+    out = torch.empty((b.rows, int(cache.desc.num_heads), 128), dtype=torch.float16, device=dev)
+
+    def step():
+        for l in range(NL):
+            pkv.append(cache, l, k, v, pos, rot, tables, stream=stream)
+            pkv.decode_attention(cache, l, out, q, tables, lens, maxL, SCALE, ws, stream=stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tokens = float(b.context_lens.sum())
+    return {
+        "workload": "13 rows x 8,192 tokens, 32 layers (append + decode per layer), 60 GB pool",
+        "ms_per_step": ms,
+        "kv_tokens_per_s": tokens / (ms / 1e3),
+        "hbm_tb_s": tokens * STEP_TOKEN_BYTES / (ms / 1e3) / 1e12,
+        "hbm_frac_of_peak": tokens * STEP_TOKEN_BYTES / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+    }
 
 
 def log(args, msg):
@@ -381,6 +472,12 @@ def main():
                         "sample": f"fp64 oracle decode of {rows_done} (row, layer-0) tasks of the same step, "
                                   f"{tok_done} one-layer tokens in {cpu_s:.1f} s; value = layer-tokens / 32 / s"}
 
+    blocks = None
+    long_ctx = None
+    if not args.no_extra:
+        blocks = measure_block_copies(torch, pkv, cache, bp.free_list(), stream)
+        long_ctx = measure_long_context(torch, pkv, cache, stream)
+
     prefill = None
     if not args.no_prefill:
         prefill = measure_prefill(torch, pkv, dev, stream)
@@ -418,6 +515,8 @@ def main():
         "parity_step0_layer0": parity,
         "prefill": prefill,
         "trace": trace,
+        "long_context": long_ctx,
+        "block_copy": blocks,
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(rec), flush=True)

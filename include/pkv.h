@@ -223,6 +223,47 @@ int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t layer, void* o
                                   int32_t max_q_per_row, int32_t max_context_len, float scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Whole-block copies.
+ *
+ * A block with all its layers is one contiguous region of the pool of
+ * pkv_block_bytes(cache) = num_layers * 2 * num_heads * 16 * 128 * 2 bytes
+ * (8 MiB for 32 layers x 32 heads); these calls move whole blocks.
+ *
+ * Copy-on-write: requests sharing prefix blocks hold them immutable, and a
+ * branch that diverges inside a shared block takes a private copy of it
+ * first (The inference engine, wpnews.pro, "Weights, activations, and KV
+ * state occupy different ledgers" and "Paging turns variable sequences into
+ * block tables").  pkv_copy_blocks copies block src_ids[i] to dst_ids[i] for
+ * i < n, every layer, K and V, bit for bit.
+ *   src_ids, dst_ids  device int32 [n]
+ * The dst ids must be distinct and none may also be a src id of the same call
+ * (otherwise the result is unspecified).  A pair with an id outside
+ * [0, num_blocks) is skipped.  n == 0 is a no-op.  cache->base 16-byte
+ * aligned.
+ *
+ * Swap: under memory pressure a scheduler may move a sequence's blocks to
+ * host memory and restore them later instead of recomputing its prefill
+ * (Build a continuous batching server, scalablesystem.dev, "Preemption and
+ * Eviction: Recompute vs Swap"; Inference Infrastructure, seeitflow.com, "An
+ * overload example").  pkv_swap_out copies block ids[i] to
+ * host_dst + i * pkv_block_bytes(cache); pkv_swap_in copies
+ * host_src + i * pkv_block_bytes(cache) to block ids[i].
+ *   ids                host int32 [n], each in [0, num_blocks), else
+ *                      PKV_ERR_BAD_BLOCK and nothing is queued
+ *   host_dst/host_src  host memory of n * pkv_block_bytes(cache) bytes; pinned
+ *                      (hipHostMalloc) for the copy to be asynchronous
+ * The copies are queued on `stream` (one DMA copy per run of consecutive
+ * ids); the host buffer must stay valid until they finish.  pkv_swap_in's ids
+ * must be distinct.  If the HIP runtime refuses a copy after earlier runs
+ * were queued, those runs stay queued and PKV_ERR_HIP is returned.
+ * ---------------------------------------------------------------------- */
+size_t pkv_block_bytes(const pkv_cache* cache); /* 0 for an invalid descriptor */
+int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids, const int32_t* dst_ids, int32_t n,
+                    void* stream);
+int pkv_swap_out(const pkv_cache* cache, const int32_t* ids, int32_t n, void* host_dst, void* stream);
+int pkv_swap_in(const pkv_cache* cache, const void* host_src, const int32_t* ids, int32_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

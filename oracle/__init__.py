@@ -12,9 +12,11 @@ Contents
           with per-block reference counts.
   brute   pure-Python attention over contiguous key/value lists, for tiny
           inputs only.
+  blocks  whole-block copies: copy-on-write inside the pool, swap out to and
+          in from a host image.
 
 Pins (what holds this oracle to something other than itself) live in
 tests/test_oracle_*.py: the pages' printed block arithmetic, closed forms,
 invariants and the brute force.  No function here is "parity unpinned".
 """
-from . import brute, paged, pool  # noqa: F401
+from . import blocks, brute, paged, pool  # noqa: F401

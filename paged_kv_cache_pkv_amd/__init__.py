@@ -197,3 +197,45 @@ def chunked_prefill_attention(cache: PagedCache, layer: int, out, q, query_start
         _dptr(query_start, "query_start", 4), _dptr(block_tables, "block_tables", 4), stride,
         _dptr(context_lens, "context_lens", 4), R, T, int(max_q_per_row), int(max_context_len), float(scale),
         _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+
+
+# ------------------------------------------------------------------ whole blocks
+
+def block_bytes(cache: PagedCache) -> int:
+    """Bytes of one block with all its layers (one contiguous region of the pool)."""
+    return int(lib().pkv_block_bytes(ctypes.byref(cache.desc)))
+
+
+def copy_blocks(cache: PagedCache, src_ids, dst_ids, stream=None):
+    """Copy-on-write: block src_ids[i] -> dst_ids[i], all layers (device int32 tensors)."""
+    n = int(src_ids.numel())
+    if int(dst_ids.numel()) != n:
+        raise ValueError("src_ids and dst_ids must have the same length")
+    _check(lib().pkv_copy_blocks(ctypes.byref(cache.desc), _dptr(src_ids, "src_ids", 4), _dptr(dst_ids, "dst_ids", 4),
+                                 n, _stream_ptr(stream)))
+
+
+def _host_buf(t, need: int, what: str):
+    if t.is_cuda:
+        raise ValueError(f"{what} must be host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"{what} holds {t.numel() * t.element_size()} bytes, needs {need}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def swap_out(cache: PagedCache, ids, host_dst, stream=None):
+    """Queue copies of blocks ids (host ints) into host_dst (a pinned host tensor),
+    block i at byte offset i * block_bytes(cache)."""
+    a = _i32(ids)
+    buf = _host_buf(host_dst, len(a) * block_bytes(cache), "host_dst")
+    _check(lib().pkv_swap_out(ctypes.byref(cache.desc), _iptr(a), len(a), buf, _stream_ptr(stream)))
+
+
+def swap_in(cache: PagedCache, host_src, ids, stream=None):
+    """Queue copies of host_src (a pinned host tensor), block i at byte offset
+    i * block_bytes(cache), into blocks ids (host ints)."""
+    a = _i32(ids)
+    buf = _host_buf(host_src, len(a) * block_bytes(cache), "host_src")
+    _check(lib().pkv_swap_in(ctypes.byref(cache.desc), buf, _iptr(a), len(a), _stream_ptr(stream)))

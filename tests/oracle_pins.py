@@ -21,6 +21,7 @@ import os
 
 import numpy as np
 
+import oracle.blocks as oblocks
 import oracle.brute as brute
 import oracle.paged as paged
 import oracle.pool as opool
@@ -321,5 +322,71 @@ def pin_invariants(seed=16):
                                rtol=0, atol=1e-14)
 
 
+def pin_copy_on_write_divergence(seed=17):
+    """Two branches share a 20-token prefix (one full block and one partial
+    block, both layers).  Branch B copies the partial block before writing its
+    own token 20 into the copy; branch A writes its token 20 into the shared
+    original.  Each branch's decode, in both layers, must equal brute-force
+    attention over its own contiguous context, which never passed through a
+    block table or a copy."""
+    rng = np.random.default_rng(seed)
+    NB, NL, H, D = 10, 2, 2, 8
+    a_blk, b_blk, c_blk = 6, 2, 9
+    prefix = [_rand_bits(rng, (2, H, 20, D)) for _ in range(NL)]  # per layer: K, V of the shared prefix
+    tokA = [_rand_bits(rng, (2, H, 1, D)) for _ in range(NL)]
+    tokB = [_rand_bits(rng, (2, H, 1, D)) for _ in range(NL)]
+    pool = None
+    for l in range(NL):
+        lay = _page_in_flat(NB, NL, H, D, l, [a_blk, b_blk], prefix[l][0], prefix[l][1])
+        pool = lay if pool is None else pool
+        pool[:, l] = lay[:, l]
+    pool = oblocks.copy_blocks(pool, [b_blk], [c_blk])
+    tables = np.array([[a_blk, b_blk], [a_blk, c_blk]], dtype=np.int32)
+    for l in range(NL):
+        kn = np.stack([tokA[l][0][:, 0], tokB[l][0][:, 0]])
+        vn = np.stack([tokA[l][1][:, 0], tokB[l][1][:, 0]])
+        pool = paged.append(pool, l, kn, vn, [20, 20], [0, 1], tables)
+    q = _rand_bits(rng, (2, H, D))
+    for l in range(NL):
+        got = paged.decode(pool[:, l], q, tables, [21, 21], 0.25)
+        for r, tok in enumerate((tokA, tokB)):
+            K = np.concatenate([prefix[l][0], tok[l][0]], axis=1)
+            V = np.concatenate([prefix[l][1], tok[l][1]], axis=1)
+            for h in range(H):
+                ref = brute.attend_one(_f64(q[r, h]).tolist(), _f64(K[h]).tolist(), _f64(V[h]).tolist(), 0.25)
+                np.testing.assert_allclose(got[r, h], ref, rtol=0, atol=1e-12)
+
+
+def pin_swap_roundtrip(seed=18):
+    """A host image holds each swapped block as the block's flat element range
+    (checked with the independent offset formula), and restoring it at other
+    physical ids, with the table remapped, leaves every decode output equal
+    bit for bit, in every layer."""
+    rng = np.random.default_rng(seed)
+    NB, NL, H, D = 12, 2, 2, 8
+    pool = _rand_bits(rng, (NB, NL, 2, H, 16, D))
+    ids = [3, 7, 8, 1]
+    host = oblocks.swap_out(pool, ids)
+    flat = pool.reshape(-1)
+    host_flat = host.reshape(len(ids), -1)
+    per_block = NL * 2 * H * 16 * D
+    assert host_flat.shape[1] == per_block
+    for i, b in enumerate(ids):
+        for l, kv, h, s_, d in ((0, 0, 0, 0, 0), (1, 1, 1, 15, D - 1), (1, 0, 1, 7, 3), (0, 1, 0, 9, 5)):
+            assert host_flat[i, flat_offset(0, l, kv, h, s_, d, NL, H, D)] == flat[flat_offset(b, l, kv, h, s_, d, NL, H, D)]
+    new_ids = [5, 0, 11, 2]
+    poisoned = pool.copy()
+    poisoned[new_ids] = np.uint16(0x7E00)
+    restored = oblocks.swap_in(poisoned, host, new_ids)
+    remap = {o: n for o, n in zip(ids, new_ids)}
+    tables = np.array([[3, 7], [8, 1]], dtype=np.int32)
+    tables2 = np.vectorize(remap.get)(tables).astype(np.int32)
+    q = _rand_bits(rng, (2, H, D))
+    for l in range(NL):
+        np.testing.assert_array_equal(paged.decode(restored[:, l], q, tables2, [29, 20], 0.25),
+                                      paged.decode(pool[:, l], q, tables, [29, 20], 0.25))
+
+
 ALL_PINS = [pin_block_arithmetic, pin_pool_capacity, pin_pool_semantics, pin_append_offsets,
-            pin_gather_roundtrip, pin_bruteforce, pin_closed_forms, pin_decode_reads_own_token, pin_invariants]
+            pin_gather_roundtrip, pin_bruteforce, pin_closed_forms, pin_decode_reads_own_token, pin_invariants,
+            pin_copy_on_write_divergence, pin_swap_roundtrip]

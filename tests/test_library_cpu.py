@@ -202,3 +202,28 @@ def test_validation_append_args():
     assert L.pkv_append(ctypes.byref(d), 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, 16, None) == -1
     assert L.pkv_append(ctypes.byref(d), 0, None, FAKE, FAKE, FAKE, 4, FAKE, 4, 16, None) == -1
     assert L.pkv_append(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 16, None) == -1
+
+
+def test_validation_block_copies():
+    L = pkv.lib()
+    d = _desc(num_layers=3, num_heads=5)
+    assert L.pkv_block_bytes(ctypes.byref(d)) == 3 * 2 * 5 * 16 * 128 * 2
+    bad = _desc(head_dim=64)
+    assert L.pkv_block_bytes(ctypes.byref(bad)) == 0
+    # copy-on-write pairs live on the device: only the scalars are checked here
+    assert L.pkv_copy_blocks(ctypes.byref(d), FAKE, FAKE, 0, None) == 0  # empty = no-op
+    assert L.pkv_copy_blocks(ctypes.byref(d), FAKE, FAKE, -1, None) == -1
+    assert L.pkv_copy_blocks(ctypes.byref(d), None, FAKE, 2, None) == -1
+    assert L.pkv_copy_blocks(ctypes.byref(bad), FAKE, FAKE, 2, None) == -2
+    # swap ids live on the host and are all checked before anything is queued
+    ids = np.array([3, 64, 1], dtype=np.int32)
+    p = ids.ctypes.data_as(_lib.c_i32_p)
+    assert L.pkv_swap_out(ctypes.byref(d), p, 3, FAKE, None) == -5
+    assert b"64" in L.pkv_last_error()
+    assert L.pkv_swap_in(ctypes.byref(d), FAKE, p, 3, None) == -5
+    neg = np.array([-1], dtype=np.int32)
+    assert L.pkv_swap_in(ctypes.byref(d), FAKE, neg.ctypes.data_as(_lib.c_i32_p), 1, None) == -5
+    assert L.pkv_swap_out(ctypes.byref(d), p, 0, FAKE, None) == 0
+    assert L.pkv_swap_out(ctypes.byref(d), p, -2, FAKE, None) == -1
+    assert L.pkv_swap_out(ctypes.byref(d), p, 1, None, None) == -1
+    assert L.pkv_swap_in(ctypes.byref(d), None, p, 1, None) == -1

@@ -4,6 +4,7 @@ oracle rather than restating it."""
 import numpy as np
 import pytest
 
+import oracle.blocks as oblocks
 import oracle.paged as paged
 import oracle.pool as opool
 from tests import oracle_pins
@@ -90,3 +91,36 @@ def test_pool_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(opool, "blocks_needed", _blocks_floor)
     with pytest.raises(AssertionError):
         oracle_pins.pin_block_arithmetic()
+
+
+_copy_blocks = oblocks.copy_blocks
+_swap_in = oblocks.swap_in
+
+
+def _copy_first_layer_only(pool, src, dst):
+    out = _copy_blocks(pool, src, dst)
+    for d in np.asarray(dst).tolist():
+        out[d, 1:] = pool[d, 1:]
+    return out
+
+
+def _copy_wrong_direction(pool, src, dst):
+    return _copy_blocks(pool, dst, src)
+
+
+def _swap_in_reversed(pool, host, ids):
+    return _swap_in(pool, host, list(ids)[::-1])
+
+
+@pytest.mark.parametrize("name,fn", [("copy_blocks", _copy_first_layer_only), ("copy_blocks", _copy_wrong_direction),
+                                     ("swap_in", _swap_in_reversed)],
+                         ids=["copy_first_layer_only", "copy_wrong_direction", "swap_in_reversed"])
+def test_blocks_mutant_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(oblocks, name, fn)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {fn.__name__}"
