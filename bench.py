@@ -284,6 +284,53 @@ def measure_long_context(torch, pkv, cache, stream, steps=5, warm=2):
     }
 
 
+def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, warm=3):
+    """Grouped-query decode: the average mix's tables and lengths over a
+    32-layer pool of 8 KV heads (2 MiB blocks), 32 query heads (groups of 4);
+    per layer one decode launch.  Bytes = K and V of 8 heads per token."""
+    from workloads import SCALE, fill_normal_fp16_device
+
+    NB, NL = 7152, 32
+    dev = torch.device("cuda", 0)
+    pool = torch.empty((NB, NL, 2, kv_heads, 16, 128), dtype=torch.int16, device=dev)
+    fill_normal_fp16_device(pool, seed=3003)
+    cache = pkv.PagedCache(pool)
+    tables = torch.from_numpy(batch.block_tables).to(dev)
+    lens = torch.from_numpy(batch.context_lens.astype(np.int32)).to(dev)
+    R = batch.rows
+    maxL = int(batch.context_lens.max())
+    rng = np.random.default_rng(3004)
+    q = torch.from_numpy(rng.standard_normal((NL, R, q_heads, 128), dtype=np.float32).astype(np.float16)).to(dev)
+    out = torch.empty((R, q_heads, 128), dtype=torch.float16, device=dev)
+    ws = torch.empty(pkv.decode_workspace_size_gqa(cache, q_heads, R, maxL), dtype=torch.uint8, device=dev)
+
+    def step():
+        for l in range(NL):
+            pkv.decode_attention_gqa(cache, q_heads, l, out, q[l], tables, lens, maxL, SCALE, ws, stream=stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tokens = float(batch.context_lens.sum())
+    kv_bytes = tokens * NL * 2 * kv_heads * 128 * 2
+    del pool
+    return {
+        "workload": f"average-mix decode with grouped-query attention: {R} rows x {NL} layers, {kv_heads} KV heads, "
+                    f"{q_heads} query heads, FP16, {NB} blocks of 16",
+        "ms_per_step": ms,
+        "kv_tokens_per_s": tokens / (ms / 1e3),
+        "hbm_tb_s": kv_bytes / (ms / 1e3) / 1e12,
+        "hbm_frac_of_peak": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
 def log(args, msg):
     if not args.quiet:
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -474,9 +521,11 @@ def main():
 
     blocks = None
     long_ctx = None
+    gqa = None
     if not args.no_extra:
         blocks = measure_block_copies(torch, pkv, cache, bp.free_list(), stream)
         long_ctx = measure_long_context(torch, pkv, cache, stream)
+        gqa = measure_gqa(torch, pkv, batch, stream)
 
     prefill = None
     if not args.no_prefill:
@@ -516,6 +565,7 @@ def main():
         "prefill": prefill,
         "trace": trace,
         "long_context": long_ctx,
+        "gqa_decode": gqa,
         "block_copy": blocks,
         "cpu_baseline": cpu_baseline,
     }

@@ -224,6 +224,41 @@ int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t layer, void* o
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped-query attention.
+ *
+ * The number of KV heads, not of query heads, sets the cache size; grouped-
+ * query attention shares one K/V head among a group of query heads
+ * (Inference Infrastructure, seeitflow.com: the KV-bytes formula and its
+ * MHA / MQA / GQA note; The inference engine, wpnews.pro: grouped-query
+ * attention lowers the KV-head count below the query-head count).  The pool
+ * descriptor's num_heads is the number of KV heads; num_q_heads =
+ * G * num_heads query heads attend, and query head h reads KV head h / G
+ * (consecutive query heads form a group).  q and out are
+ * [rows or tokens][num_q_heads][128]; everything else is as in
+ * pkv_decode_attention / pkv_chunked_prefill_attention, which are these calls
+ * with num_q_heads = num_heads.
+ *   decode: G in {1, 2, 4, 8}, else PKV_ERR_UNSUPPORTED.  One wave reads a KV
+ *           head's keys and values once for all G query heads.
+ *   prefill: any G with num_q_heads <= 1024.  Each query head's tile reads
+ *           its group's K/V tile (from cache when the group's tiles run
+ *           together); decode rows of the launch likewise.
+ * The workspace sizes count query heads.
+ * ---------------------------------------------------------------------- */
+size_t pkv_decode_workspace_size_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t num_rows,
+                                     int32_t max_context_len);
+int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out, const void* q,
+                             const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                             int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+size_t pkv_prefill_workspace_size_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t num_rows,
+                                      int32_t total_q, int32_t max_q_per_row, int32_t max_context_len);
+int pkv_chunked_prefill_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,
+                                      const void* q, const int32_t* query_start, const int32_t* block_tables,
+                                      int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
+                                      int32_t total_q, int32_t max_q_per_row, int32_t max_context_len, float scale,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole-block copies.
  *
  * A block with all its layers is one contiguous region of the pool of

@@ -116,26 +116,40 @@ def attention(q, K, V, query_positions, scale: float) -> np.ndarray:
     return out
 
 
-def decode(pool_layer, q, block_tables, context_lens, scale: float, rows=None) -> np.ndarray:
+def group_kv(K, V, group: int):
+    """Keys and values as seen by each query head under grouped-query
+    attention: one K/V head is shared by a group of `group` query heads
+    (Inference Infrastructure, seeitflow: MHA keeps one K/V pair per query
+    head, GQA shares one K/V head among a group of query heads).  The pages do
+    not say which query heads form a group; consecutive heads do here, so query
+    head h reads KV head h // group.  group = 1 is plain multi-head attention."""
+    if group == 1:
+        return K, V
+    return np.repeat(K, group, axis=0), np.repeat(V, group, axis=0)
+
+
+def decode(pool_layer, q, block_tables, context_lens, scale: float, rows=None, group: int = 1) -> np.ndarray:
     """One query per row at position context_lens[r] - 1, over that row's
-    gathered context.  q is [R, heads, head_dim]; returns [R, heads, head_dim]
+    gathered context.  q is [R, heads * group, head_dim]; returns that shape
     (or only the listed rows, in the order given)."""
     rows = range(len(context_lens)) if rows is None else rows
     outs = []
     for r in rows:
         L = int(context_lens[r])
-        K, V = gather_kv(pool_layer, block_tables[r], L)
+        K, V = group_kv(*gather_kv(pool_layer, block_tables[r], L), group)
         outs.append(attention(np.asarray(q)[r:r + 1], K, V, [L - 1], scale)[0])
     return np.stack(outs)
 
 
-def chunked_prefill(pool_layer, q, query_start, block_tables, context_lens, scale: float, rows=None) -> np.ndarray:
+def chunked_prefill(pool_layer, q, query_start, block_tables, context_lens, scale: float, rows=None,
+                    group: int = 1) -> np.ndarray:
     """Row r owns queries query_start[r] .. query_start[r+1]-1, which are the last
     n_r positions of its context, L_r - n_r .. L_r - 1.  A row with n_r = 1 is
     a decode row.  Prefill chunks and decode rows share one step as a flat list
     of tokens tagged with their request (LLM inference batching, faangrind,
-    "Prefill and decode share each step").  Returns [T, heads, head_dim], or for
-    `rows` the concatenation of those rows' query outputs."""
+    "Prefill and decode share each step").  q has heads * group query heads
+    (see group_kv).  Returns [T, heads * group, head_dim], or for `rows` the
+    concatenation of those rows' query outputs."""
     qs = np.asarray(query_start)
     rows = range(len(context_lens)) if rows is None else rows
     outs = []
@@ -143,6 +157,6 @@ def chunked_prefill(pool_layer, q, query_start, block_tables, context_lens, scal
         L = int(context_lens[r])
         a, b = int(qs[r]), int(qs[r + 1])
         n = b - a
-        K, V = gather_kv(pool_layer, block_tables[r], L)
+        K, V = group_kv(*gather_kv(pool_layer, block_tables[r], L), group)
         outs.append(attention(np.asarray(q)[a:b], K, V, np.arange(L - n, L), scale))
     return np.concatenate(outs, axis=0)

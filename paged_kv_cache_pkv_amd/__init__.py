@@ -171,29 +171,52 @@ def decode_workspace_size(cache: PagedCache, num_rows: int, max_context_len: int
     return int(lib().pkv_decode_workspace_size(ctypes.byref(cache.desc), int(num_rows), int(max_context_len)))
 
 
+def decode_workspace_size_gqa(cache: PagedCache, num_q_heads: int, num_rows: int, max_context_len: int) -> int:
+    return int(lib().pkv_decode_workspace_size_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(num_rows),
+                                                   int(max_context_len)))
+
+
 def decode_attention(cache: PagedCache, layer: int, out, q, block_tables, context_lens, max_context_len: int,
                      scale: float, workspace=None, stream=None):
+    decode_attention_gqa(cache, cache.num_heads, layer, out, q, block_tables, context_lens, max_context_len, scale,
+                         workspace, stream)
+
+
+def decode_attention_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q, block_tables, context_lens,
+                         max_context_len: int, scale: float, workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_decode_attention(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2),
-                                      _dptr(block_tables, "block_tables", 4), stride,
-                                      _dptr(context_lens, "context_lens", 4), R, int(max_context_len), float(scale),
-                                      _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+    _check(lib().pkv_decode_attention_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(layer), _dptr(out, "out", 2),
+                                          _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,
+                                          _dptr(context_lens, "context_lens", 4), R, int(max_context_len),
+                                          float(scale), _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
 
 
 def prefill_workspace_size(cache: PagedCache, num_rows: int, total_q: int, max_q_per_row: int,
                            max_context_len: int) -> int:
-    return int(lib().pkv_prefill_workspace_size(ctypes.byref(cache.desc), int(num_rows), int(total_q),
-                                                int(max_q_per_row), int(max_context_len)))
+    return prefill_workspace_size_gqa(cache, cache.num_heads, num_rows, total_q, max_q_per_row, max_context_len)
+
+
+def prefill_workspace_size_gqa(cache: PagedCache, num_q_heads: int, num_rows: int, total_q: int, max_q_per_row: int,
+                               max_context_len: int) -> int:
+    return int(lib().pkv_prefill_workspace_size_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(num_rows),
+                                                    int(total_q), int(max_q_per_row), int(max_context_len)))
 
 
 def chunked_prefill_attention(cache: PagedCache, layer: int, out, q, query_start, block_tables, context_lens,
                               max_q_per_row: int, max_context_len: int, scale: float, workspace=None, stream=None):
+    chunked_prefill_attention_gqa(cache, cache.num_heads, layer, out, q, query_start, block_tables, context_lens,
+                                  max_q_per_row, max_context_len, scale, workspace, stream)
+
+
+def chunked_prefill_attention_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q, query_start, block_tables,
+                                  context_lens, max_q_per_row: int, max_context_len: int, scale: float,
+                                  workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)
     T = int(q.shape[0])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_chunked_prefill_attention(
-        ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2),
+    _check(lib().pkv_chunked_prefill_attention_gqa(
+        ctypes.byref(cache.desc), int(num_q_heads), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2),
         _dptr(query_start, "query_start", 4), _dptr(block_tables, "block_tables", 4), stride,
         _dptr(context_lens, "context_lens", 4), R, T, int(max_q_per_row), int(max_context_len), float(scale),
         _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))

@@ -46,13 +46,14 @@ constexpr int kXcds = 8;
 
 struct DecodeArgs {
   const uint16_t* pool;
-  const uint4* q;       // [R][H][16] chunks of 8 halves
-  uint4* out;           // [R][H][16]
+  const uint4* q;       // [R][Hq][16] chunks of 8 halves
+  uint4* out;           // [R][Hq][16]
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* part_o;        // [R][H][S][128]
-  float2* part_ml;      // [R][H][S]
-  int layer, num_blocks, num_layers, num_heads;
+  float* part_o;        // [R][Hq][S][128]
+  float2* part_ml;      // [R][Hq][S]
+  int layer, num_blocks, num_layers, num_heads;  // num_heads: KV heads of the pool
+  int num_q_heads;      // num_heads * G
   int bt_stride, num_rows, max_context_len, max_splits;
   float qk_scale;       // scale * log2(e)
 };
@@ -92,18 +93,111 @@ __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_ke
                L, split, a.q + rh * 16, a.qk_scale, a.out + rh * 16, a.part_o + slot * kHeadDim, a.part_ml + slot);
 }
 
+// Grouped-query decode: G query heads share each KV head.  A workgroup of
+// kGqaWaves waves owns one (row, range, KV head); wave w folds its equal
+// share of the range's 16 blocks for all G query heads, so every key and
+// value is read once for the group, and the waves' softmax states combine
+// through LDS in wave order (The inference engine, wpnews.pro: tile
+// statistics combine exactly).  The range partition matches the decode
+// launch's, so a row's result does not depend on its batch neighbours.
+#ifndef PKV_GQA_WAVES
+#define PKV_GQA_WAVES 4
+#endif
+#ifndef PKV_GQA_DEPTH
+#define PKV_GQA_DEPTH 3
+#endif
+constexpr int kGqaWaves = PKV_GQA_WAVES;
+constexpr int kGqaThreads = 64 * kGqaWaves;
+static_assert(kSplitBlocks % kGqaWaves == 0, "each wave takes an equal share of a range");
+
+template <int G>
+__global__ __launch_bounds__(kGqaThreads) void decode_gqa_kernel(DecodeArgs a) {
+  __shared__ float s_m[kGqaWaves][G], s_l[kGqaWaves][G];
+  __shared__ float4 s_o[kGqaWaves][G][32];
+  const int n = blockIdx.x;
+#if PKV_XCD_REMAP
+  // the KV heads of one (row, range) run back to back on one XCD
+  const int m = n / kXcds;
+  const int h = m % a.num_heads;
+  const int rs = (n % kXcds) + kXcds * (m / a.num_heads);
+#else
+  const int h = n % a.num_heads;
+  const int rs = n / a.num_heads;
+#endif
+  const int split = rs % a.max_splits;
+  const int r = rs / a.max_splits;
+  if (r >= a.num_rows) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  int L = a.context_lens[r];
+  L = L > a.max_context_len ? a.max_context_len : L;
+  const size_t rh = (size_t)r * a.num_q_heads + (size_t)h * G;  // the KV head's first query head
+  if (L < 1) {
+    if (split == 0 && wave == 0 && lane < 16)
+#pragma unroll
+      for (int g = 0; g < G; ++g) a.out[(rh + g) * 16 + lane] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  const int nsplit = decode_splits(L);
+  if (split >= nsplit) return;
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  constexpr int kPer = kSplitBlocks / kGqaWaves;
+  const int b0 = min(nb, split * kSplitBlocks + wave * kPer);
+  const int b1 = min(nb, b0 + kPer);
+  SoftmaxState st[G];
+  fold_blocks<(G >= 8 ? 2 : PKV_GQA_DEPTH), G>(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
+                                        a.block_tables + (size_t)r * a.bt_stride, L, b0, b1, a.q + rh * 16,
+                                        a.qk_scale, st);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (lane < 16) {
+      s_o[wave][g][2 * lane] = make_float4(st[g].o[0], st[g].o[1], st[g].o[2], st[g].o[3]);
+      s_o[wave][g][2 * lane + 1] = make_float4(st[g].o[4], st[g].o[5], st[g].o[6], st[g].o[7]);
+    }
+    if (lane == 0) {
+      s_m[wave][g] = st[g].m;
+      s_l[wave][g] = st[g].l;
+    }
+  }
+  __syncthreads();
+  // wave w combines query heads g = w, w + kGqaWaves, ...; lane owns dims 2*lane, 2*lane + 1
+  for (int g = wave; g < G; g += kGqaWaves) {
+    float M = kMinusBig;
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) {
+      const float f = fast_exp2(s_m[w][g] - M);
+      const float2 v = reinterpret_cast<const float2*>(&s_o[w][g][0])[lane];
+      l = fmaf(s_l[w][g], f, l);
+      o0 = fmaf(v.x, f, o0);
+      o1 = fmaf(v.y, f, o1);
+    }
+    const size_t hq = rh + g;
+    if (nsplit == 1) {
+      const float inv = 1.0f / l;
+      reinterpret_cast<uint32_t*>(a.out)[hq * 64 + lane] = pack_half2(o0 * inv, o1 * inv);
+    } else {
+      const size_t slot = hq * a.max_splits + split;
+      reinterpret_cast<float2*>(a.part_o + slot * kHeadDim)[lane] = make_float2(o0, o1);
+      if (lane == 0) a.part_ml[slot] = make_float2(M, l);
+    }
+  }
+}
+
 // Merge the ranges of every (row, head) that has more than one; one wave per
 // (row, head).
 __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeArgs a) {
   const int r = blockIdx.x;
-  const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kWavesPerGroup + (threadIdx.x >> 6));
-  if (h >= a.num_heads) return;
+  const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kWavesPerGroup + (threadIdx.x >> 6));  // query head
+  if (h >= a.num_q_heads) return;
   int L = a.context_lens[r];
   L = L > a.max_context_len ? a.max_context_len : L;
   if (L < 1) return;
   const int nsplit = decode_splits(L);
   if (nsplit <= 1) return;
-  const size_t rh = (size_t)r * a.num_heads + h;
+  const size_t rh = (size_t)r * a.num_q_heads + h;
   merge_partials(a.part_o + rh * a.max_splits * kHeadDim, a.part_ml + rh * a.max_splits, nsplit,
                  reinterpret_cast<uint32_t*>(a.out) + rh * 64);
 }
@@ -115,20 +209,48 @@ int max_splits_for(int32_t max_context_len) { return decode_splits(max_context_l
 
 extern "C" int32_t pkv_split_tokens(void) { return pkv::kSplitBlocks * pkv::kBlockSize; }
 
-extern "C" size_t pkv_decode_workspace_size(const pkv_cache* cache, int32_t num_rows, int32_t max_context_len) {
+namespace pkv {
+namespace {
+
+int group_of(const pkv_cache* cache, int32_t num_q_heads) {
+  if (num_q_heads < 1 || num_q_heads % cache->num_heads) return 0;
+  const int g = num_q_heads / cache->num_heads;
+  return (g == 1 || g == 2 || g == 4 || g == 8) ? g : 0;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" size_t pkv_decode_workspace_size_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t num_rows,
+                                                int32_t max_context_len) {
   using namespace pkv;
-  if (!cache || num_rows < 1 || max_context_len < 1 || cache->num_heads < 1) return 0;
+  if (!cache || num_rows < 1 || max_context_len < 1 || cache->num_heads < 1 || num_q_heads < 1) return 0;
   const size_t s = (size_t)max_splits_for(max_context_len);
-  const size_t n = (size_t)num_rows * cache->num_heads * s;
+  const size_t n = (size_t)num_rows * num_q_heads * s;
   return align256(n * kHeadDim * sizeof(float)) + align256(n * sizeof(float2));
+}
+
+extern "C" size_t pkv_decode_workspace_size(const pkv_cache* cache, int32_t num_rows, int32_t max_context_len) {
+  return cache ? pkv_decode_workspace_size_gqa(cache, cache->num_heads, num_rows, max_context_len) : 0;
 }
 
 extern "C" int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void* out, const void* q,
                                     const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
                                     int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
                                     size_t workspace_bytes, void* stream) {
+  if (!cache) return pkv::fail(PKV_ERR_INVALID_ARG, "cache is null");
+  return pkv_decode_attention_gqa(cache, cache->num_heads, layer, out, q, block_tables, bt_stride, context_lens,
+                                  num_rows, max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,
+                                        const void* q, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* context_lens, int32_t num_rows, int32_t max_context_len,
+                                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pkv;
   if (int rc = check_cache(cache)) return rc;
+  const int G = group_of(cache, num_q_heads);
+  if (!G) return fail(PKV_ERR_UNSUPPORTED, "num_q_heads must be 1, 2, 4 or 8 times the pool's KV heads");
   if (layer < 0 || layer >= cache->num_layers) return fail(PKV_ERR_INVALID_ARG, "layer out of range");
   if (num_rows < 1) return fail(PKV_ERR_INVALID_ARG, "num_rows must be >= 1");
   if (!out || !q || !block_tables || !context_lens) return fail(PKV_ERR_INVALID_ARG, "null device pointer");
@@ -140,7 +262,7 @@ extern "C" int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void*
        reinterpret_cast<uintptr_t>(cache->base)) & 15)
     return fail(PKV_ERR_INVALID_ARG, "out, q and cache->base must be 16-byte aligned");
   const int ms = max_splits_for(max_context_len);
-  const size_t need = pkv_decode_workspace_size(cache, num_rows, max_context_len);
+  const size_t need = pkv_decode_workspace_size_gqa(cache, num_q_heads, num_rows, max_context_len);
   if (ms > 1) {
     if (!workspace || workspace_bytes < need)
       return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
@@ -152,7 +274,7 @@ extern "C" int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void*
   a.out = static_cast<uint4*>(out);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  const size_t n = (size_t)num_rows * cache->num_heads * ms;
+  const size_t n = (size_t)num_rows * num_q_heads * ms;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = workspace ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + align256(n * kHeadDim * sizeof(float)))
                         : nullptr;
@@ -160,23 +282,35 @@ extern "C" int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void*
   a.num_blocks = cache->num_blocks;
   a.num_layers = cache->num_layers;
   a.num_heads = cache->num_heads;
+  a.num_q_heads = num_q_heads;
   a.bt_stride = bt_stride;
   a.num_rows = num_rows;
   a.max_context_len = max_context_len;
   a.max_splits = ms;
   a.qk_scale = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int head_groups = (cache->num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
   int64_t rs_total = (int64_t)num_rows * ms;
 #if PKV_XCD_REMAP
   rs_total = (rs_total + kXcds - 1) / kXcds * kXcds;
 #endif
-  const int64_t wgs = rs_total * head_groups;
-  if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-  decode_split_kernel<<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
+  if (G == 1) {
+    const int head_groups = (cache->num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t wgs = rs_total * head_groups;
+    if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+    decode_split_kernel<<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
+  } else {
+    const int64_t wgs = rs_total * cache->num_heads;
+    if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+    switch (G) {
+      case 2: decode_gqa_kernel<2><<<dim3((unsigned)wgs), dim3(kGqaThreads), 0, s>>>(a); break;
+      case 4: decode_gqa_kernel<4><<<dim3((unsigned)wgs), dim3(kGqaThreads), 0, s>>>(a); break;
+      default: decode_gqa_kernel<8><<<dim3((unsigned)wgs), dim3(kGqaThreads), 0, s>>>(a); break;
+    }
+  }
   if (int rc = check_launch("decode split kernel")) return rc;
   if (ms > 1) {
-    decode_merge_kernel<<<dim3(num_rows, head_groups), dim3(kDecodeThreads), 0, s>>>(a);
+    const int q_groups = (num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+    decode_merge_kernel<<<dim3(num_rows, q_groups), dim3(kDecodeThreads), 0, s>>>(a);
     if (int rc = check_launch("decode merge kernel")) return rc;
   }
   return PKV_OK;

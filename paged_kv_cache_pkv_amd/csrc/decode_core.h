@@ -56,42 +56,53 @@ struct SoftmaxState {
   float o[8];
 };
 
-// Fold one block's four tokens (of this lane's group) into the state.
+// Fold one block's four tokens (of this lane's group) into the states of G
+// queries that share the block's keys and values (the query heads of one KV
+// head; G = 1 without grouping).  The values are unpacked once for all G.
 // valid = number of live tokens in the block (16 unless it is the last one).
-__device__ __forceinline__ void fold_tile(SoftmaxState& st, KVTile& t, const uint4& q, float qk_scale, int group,
+template <int G>
+__device__ __forceinline__ void fold_tile(SoftmaxState* st, KVTile& t, const uint4* q, float qk_scale, int group,
                                           int valid) {
-  float s[4];
+  float s[G][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = sum16(dot8(q, t.k[i])) * qk_scale;
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[g][i] = sum16(dot8(q[g], t.k[i])) * qk_scale;
   if (valid < kBlockSize) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (group + 4 * i >= valid) {
-        s[i] = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[g][i] = -INFINITY;
         t.v[i] = make_uint4(0u, 0u, 0u, 0u);  // stale slots may hold NaN; 0 * NaN would leak
       }
     }
   }
-  const float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  const float mn = fmaxf(st.m, mb);
-  const float alpha = fast_exp2(st.m - mn);
-  float p[4];
+  float p[G][4], alpha[G];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - mn);
-  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  for (int g = 0; g < G; ++g) {
+    const float mb = fmaxf(fmaxf(s[g][0], s[g][1]), fmaxf(s[g][2], s[g][3]));
+    const float mn = fmaxf(st[g].m, mb);
+    alpha[g] = fast_exp2(st[g].m - mn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[g][i] = fast_exp2(s[g][i] - mn);
+    st[g].l = st[g].l * alpha[g] + ((p[g][0] + p[g][1]) + (p[g][2] + p[g][3]));
+    st[g].m = mn;
+  }
   float v[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) unpack8(t.v[i], v[i]);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float acc = st.o[e] * alpha;
-    acc = fmaf(p[0], v[0][e], acc);
-    acc = fmaf(p[1], v[1][e], acc);
-    acc = fmaf(p[2], v[2][e], acc);
-    acc = fmaf(p[3], v[3][e], acc);
-    st.o[e] = acc;
-  }
-  st.m = mn;
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = st[g].o[e] * alpha[g];
+      acc = fmaf(p[g][0], v[0][e], acc);
+      acc = fmaf(p[g][1], v[1][e], acc);
+      acc = fmaf(p[g][2], v[2][e], acc);
+      acc = fmaf(p[g][3], v[3][e], acc);
+      st[g].o[e] = acc;
+    }
 }
 
 // Merge the four 16-lane groups' states; every lane ends with the same bits.
@@ -112,41 +123,43 @@ __device__ __forceinline__ void merge_groups(SoftmaxState& st) {
   st.m = M;
 }
 
-// Fold range `split` (blocks [split*kSplitBlocks, ...) of a context of L >= 1
-// tokens) for head h on one wave.  With a single range for the row the
-// normalised FP16 output goes to out_head (16 chunks of 8 halves); otherwise the
-// unnormalised partial goes to part_o (128 floats) and (m, l) to *part_ml.
-__device__ __forceinline__ void decode_range(const uint16_t* __restrict__ pool, int layer, int num_blocks,
-                                             int num_layers, int num_heads, int h,
-                                             const int32_t* __restrict__ row_table, int L, int split,
-                                             const uint4* __restrict__ q_head, float qk_scale,
-                                             uint4* __restrict__ out_head, float* __restrict__ part_o,
-                                             float2* __restrict__ part_ml) {
+// Fold blocks [b0, b1) (at most 64) of a context of L >= 1 tokens of KV head
+// h_kv into the softmax states of its G query heads on one wave, then merge
+// the four 16-lane groups so that every lane holds the same states.  q_head
+// points at the first query head's 16 chunks (the G heads are consecutive,
+// 16 chunks apart).  Depth = blocks whose loads are in flight per wave (plus
+// the one being folded); the fold order, and so the result, does not depend
+// on it.
+template <int Depth, int G>
+__device__ __forceinline__ void fold_blocks(const uint16_t* __restrict__ pool, int layer, int num_blocks,
+                                            int num_layers, int num_kv_heads, int h_kv,
+                                            const int32_t* __restrict__ row_table, int L, int b0, int b1,
+                                            const uint4* __restrict__ q_head, float qk_scale, SoftmaxState* st) {
   const int lane = threadIdx.x & 63;
   const int group = lane >> 4;  // token within each 4-token stripe
   const int chunk = lane & 15;  // dims 8*chunk .. 8*chunk+7
-  const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const int nsplit = (nb + kSplitBlocks - 1) / kSplitBlocks;
-  const int b0 = split * kSplitBlocks;
-  const int b1 = min(nb, b0 + kSplitBlocks);
 
-  // One vector load brings this range's block ids; readlane hands them out.
+  // One vector load brings the blocks' ids; readlane hands them out.
   const int my_id = (lane < b1 - b0) ? row_table[b0 + lane] : 0;
-  const uint4 q = q_head[chunk];
-  const int lane_off = group * kHeadDim + chunk * 8;
-  SoftmaxState st;
-  st.m = kMinusBig;
-  st.l = 0.0f;
+  uint4 q[G];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
+  for (int g = 0; g < G; ++g) q[g] = q_head[g * 16 + chunk];
+  const int lane_off = group * kHeadDim + chunk * 8;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st[g].m = kMinusBig;
+    st[g].l = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st[g].o[e] = 0.0f;
+  }
 
-  const uint16_t* head_base = pool + slab_offset(0, layer, 0, h, num_layers, num_heads);
-  const size_t block_stride = (size_t)num_layers * 2 * num_heads * kBlockSize * kHeadDim;
-  const int vdelta = num_heads * kBlockSize * kHeadDim * 2;  // bytes from a head's K tile to its V tile
+  const uint16_t* head_base = pool + slab_offset(0, layer, 0, h_kv, num_layers, num_kv_heads);
+  const size_t block_stride = (size_t)num_layers * 2 * num_kv_heads * kBlockSize * kHeadDim;
+  const int vdelta = num_kv_heads * kBlockSize * kHeadDim * 2;  // bytes from a head's K tile to its V tile
 
-  // Software pipeline: block j + kDepth - 1 is loading while block j is folded.
-  KVTile tile[kDepth];
-  bool ok[kDepth];
+  // Software pipeline: block j + Depth - 1 is loading while block j is folded.
+  KVTile tile[Depth];
+  bool ok[Depth];
   auto issue = [&](KVTile& t, bool& good, int j) {
     const int id = __builtin_amdgcn_readlane(my_id, j - b0);
     good = (unsigned)id < (unsigned)num_blocks;
@@ -154,22 +167,44 @@ __device__ __forceinline__ void decode_range(const uint16_t* __restrict__ pool, 
     load_tile(t, head_base + (size_t)safe * block_stride, vdelta, lane_off);
   };
 #pragma unroll
-  for (int u = 0; u < kDepth - 1; ++u)
+  for (int u = 0; u < Depth - 1; ++u)
     if (b0 + u < b1) issue(tile[u], ok[u], b0 + u);
-  for (int j = b0; j < b1; j += kDepth) {
+  for (int j = b0; j < b1; j += Depth) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
+    for (int u = 0; u < Depth; ++u) {
       const int jj = j + u;
-      constexpr int kAhead = kDepth - 1;
-      if (jj + kAhead < b1) issue(tile[(u + kAhead) % kDepth], ok[(u + kAhead) % kDepth], jj + kAhead);
+      constexpr int kAhead = Depth - 1;
+      if (jj + kAhead < b1) issue(tile[(u + kAhead) % Depth], ok[(u + kAhead) % Depth], jj + kAhead);
       if (jj < b1) {
         const int valid = ok[u] ? min(L - jj * kBlockSize, kBlockSize) : 0;
-        fold_tile(st, tile[u], q, qk_scale, group, valid);
+        fold_tile<G>(st, tile[u], q, qk_scale, group, valid);
       }
     }
   }
-  merge_groups(st);
+#pragma unroll
+  for (int g = 0; g < G; ++g) merge_groups(st[g]);
+}
 
+// Fold range `split` (blocks [split*kSplitBlocks, ...) of a context of L >= 1
+// tokens) for head h on one wave.  With a single range for the row the
+// normalised FP16 output goes to out_head (16 chunks of 8 halves); otherwise
+// the unnormalised partial goes to part_o (128 floats) and (m, l) to
+// *part_ml.
+template <int Depth = kDepth>
+__device__ __forceinline__ void decode_range(const uint16_t* __restrict__ pool, int layer, int num_blocks,
+                                             int num_layers, int num_heads, int h,
+                                             const int32_t* __restrict__ row_table, int L, int split,
+                                             const uint4* __restrict__ q_head, float qk_scale,
+                                             uint4* __restrict__ out_head, float* __restrict__ part_o,
+                                             float2* __restrict__ part_ml) {
+  const int lane = threadIdx.x & 63;
+  const int chunk = lane & 15;
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const int nsplit = (nb + kSplitBlocks - 1) / kSplitBlocks;
+  const int b0 = split * kSplitBlocks;
+  const int b1 = min(nb, b0 + kSplitBlocks);
+  SoftmaxState st;
+  fold_blocks<Depth, 1>(pool, layer, num_blocks, num_layers, num_heads, h, row_table, L, b0, b1, q_head, qk_scale, &st);
   if (nsplit == 1) {
     if (lane < 16) {
       const float inv = 1.0f / st.l;

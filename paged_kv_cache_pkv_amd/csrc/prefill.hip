@@ -94,7 +94,8 @@ struct PrefillArgs {
   float* part_o;               // [T][H][S][128]
   float2* part_ml;             // [T][H][S]
   int32_t* tok_splits;         // [T] ranges each query token was cut into
-  int layer, num_blocks, num_layers, num_heads;
+  int layer, num_blocks, num_layers, num_heads;  // num_heads: KV heads of the pool
+  int num_q_heads, group;      // query heads; query head h reads KV head h / group
   int bt_stride, num_rows, total_q, max_context_len, max_splits;
   int tiles_max, ranges_max;   // prefill grid factors
   int prefill_wgs;             // prefill tile workgroups (a multiple of kXcds)
@@ -236,7 +237,7 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
   }
   c.block_stride = (size_t)a.num_layers * 2 * a.num_heads * kBlockSize * kHeadDim;
   c.vdelta = (size_t)a.num_heads * kBlockSize * kHeadDim;
-  c.k_head = a.pool + slab_offset(0, a.layer, 0, h, a.num_layers, a.num_heads);
+  c.k_head = a.pool + slab_offset(0, a.layer, 0, h / a.group, a.num_layers, a.num_heads);
   c.nb = (L + kBlockSize - 1) / kBlockSize;
   c.L = L;
   c.num_blocks = a.num_blocks;
@@ -262,7 +263,7 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
   // The wave's queries as MFMA B operands: Q[wq][16k + 8*half .. +7], k = 0..7.
   h8 qf[8];
   {
-    const uint16_t* qrow = a.q + ((size_t)(qs0 + (q_ok ? wq : q_begin)) * a.num_heads + h) * kHeadDim + 8 * half;
+    const uint16_t* qrow = a.q + ((size_t)(qs0 + (q_ok ? wq : q_begin)) * a.num_q_heads + h) * kHeadDim + 8 * half;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint4 v = q_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * k) : make_uint4(0u, 0u, 0u, 0u);
@@ -450,7 +451,7 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
   const int nsplit_q = p_q / kPrefillSplit + 1;
   if (kr == 0 && h == 0 && half == 0) a.tok_splits[qs0 + wq] = nsplit_q;
   if (kr >= nsplit_q) return;
-  const size_t th = (size_t)(qs0 + wq) * a.num_heads + h;
+  const size_t th = (size_t)(qs0 + wq) * a.num_q_heads + h;
   if (nsplit_q == 1) {
     const float inv = 1.0f / lsum;
     uint16_t* orow = a.out + th * kHeadDim;
@@ -504,14 +505,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
     const int rest = logical / a.tiles_max;
     const int kr = rest % a.ranges_max;
     const int h = rest / a.ranges_max;
-    if (h >= a.num_heads) return;
+    if (h >= a.num_q_heads) return;
     int row, qtile;
     if (!find_tile(a, tile, row, qtile)) return;
     prefill_tile(a, row, qtile, h, kr);
     return;
   }
   // decode rows: (row, 256-token range, group of kPrefillWaves heads)
-  const int head_groups = (a.num_heads + kPrefillWaves - 1) / kPrefillWaves;
+  const int head_groups = (a.num_q_heads + kPrefillWaves - 1) / kPrefillWaves;
   const int d = (m - before) * kXcds + x;
   const int hg = d % head_groups;
   const int rs = d / head_groups;
@@ -519,12 +520,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
   const int h = __builtin_amdgcn_readfirstlane(hg * kPrefillWaves + (threadIdx.x >> 6));
-  if (h >= a.num_heads) return;
+  if (h >= a.num_q_heads) return;
   const int t = a.query_start[r];
   if (a.query_start[r + 1] - t != 1 || t < 0 || t >= a.total_q) return;
   int L = a.context_lens[r];
   L = L > a.max_context_len ? a.max_context_len : L;
-  const size_t th = (size_t)t * a.num_heads + h;
+  const size_t th = (size_t)t * a.num_q_heads + h;
   if (split == 0 && h == 0 && (threadIdx.x & 63) == 0) a.tok_splits[t] = L < 1 ? 1 : decode_splits(L);
   if (L < 1) {
     if (split == 0 && (threadIdx.x & 63) < 16)
@@ -533,9 +534,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
   }
   if (split >= decode_splits(L)) return;
   const size_t slot = th * a.max_splits + split;
-  decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h, a.block_tables + (size_t)r * a.bt_stride, L,
-               split, reinterpret_cast<const uint4*>(a.q) + th * 16, a.qk_scale,
-               reinterpret_cast<uint4*>(a.out) + th * 16, a.part_o + slot * kHeadDim, a.part_ml + slot);
+  // one wave per query head; with grouping, the KV head is read once per query head
+  decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h / a.group,
+               a.block_tables + (size_t)r * a.bt_stride, L, split, reinterpret_cast<const uint4*>(a.q) + th * 16,
+               a.qk_scale, reinterpret_cast<uint4*>(a.out) + th * 16, a.part_o + slot * kHeadDim, a.part_ml + slot);
 }
 
 // One wave per (query token, head): merge the token's ranges when there is
@@ -546,11 +548,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
 __global__ __launch_bounds__(kPrefillThreads) void prefill_merge_kernel(PrefillArgs a) {
   const int t = blockIdx.x;
   const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kPrefillWaves + (threadIdx.x >> 6));
-  if (h >= a.num_heads) return;
+  if (h >= a.num_q_heads) return;
   int nsplit = a.tok_splits[t];
   nsplit = nsplit > a.max_splits ? a.max_splits : nsplit;
   if (nsplit <= 1) return;
-  const size_t th = (size_t)t * a.num_heads + h;
+  const size_t th = (size_t)t * a.num_q_heads + h;
   merge_partials(a.part_o + th * a.max_splits * kHeadDim, a.part_ml + th * a.max_splits, nsplit,
                  reinterpret_cast<uint32_t*>(a.out) + th * 64);
 }
@@ -564,14 +566,21 @@ int prefill_max_splits(int32_t max_context_len) {
 }  // namespace
 }  // namespace pkv
 
-extern "C" size_t pkv_prefill_workspace_size(const pkv_cache* cache, int32_t num_rows, int32_t total_q,
-                                             int32_t max_q_per_row, int32_t max_context_len) {
+extern "C" size_t pkv_prefill_workspace_size_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t num_rows,
+                                                 int32_t total_q, int32_t max_q_per_row, int32_t max_context_len) {
   using namespace pkv;
   (void)num_rows;
   (void)max_q_per_row;
-  if (!cache || total_q < 1 || max_context_len < 1 || cache->num_heads < 1) return 0;
-  const size_t n = (size_t)total_q * cache->num_heads * prefill_max_splits(max_context_len);
+  if (!cache || total_q < 1 || max_context_len < 1 || cache->num_heads < 1 || num_q_heads < 1) return 0;
+  const size_t n = (size_t)total_q * num_q_heads * prefill_max_splits(max_context_len);
   return align256(n * kHeadDim * sizeof(float)) + align256(n * sizeof(float2)) + align256((size_t)total_q * sizeof(int32_t));
+}
+
+extern "C" size_t pkv_prefill_workspace_size(const pkv_cache* cache, int32_t num_rows, int32_t total_q,
+                                             int32_t max_q_per_row, int32_t max_context_len) {
+  return cache ? pkv_prefill_workspace_size_gqa(cache, cache->num_heads, num_rows, total_q, max_q_per_row,
+                                                max_context_len)
+               : 0;
 }
 
 extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t layer, void* out, const void* q,
@@ -579,8 +588,22 @@ extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t lay
                                              int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
                                              int32_t total_q, int32_t max_q_per_row, int32_t max_context_len,
                                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache) return pkv::fail(PKV_ERR_INVALID_ARG, "cache is null");
+  return pkv_chunked_prefill_attention_gqa(cache, cache->num_heads, layer, out, q, query_start, block_tables, bt_stride,
+                                           context_lens, num_rows, total_q, max_q_per_row, max_context_len, scale,
+                                           workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_chunked_prefill_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,
+                                                 const void* q, const int32_t* query_start,
+                                                 const int32_t* block_tables, int32_t bt_stride,
+                                                 const int32_t* context_lens, int32_t num_rows, int32_t total_q,
+                                                 int32_t max_q_per_row, int32_t max_context_len, float scale,
+                                                 void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pkv;
   if (int rc = check_cache(cache)) return rc;
+  if (num_q_heads < 1 || num_q_heads % cache->num_heads || num_q_heads > 1024)
+    return fail(PKV_ERR_UNSUPPORTED, "num_q_heads must be a multiple of the pool's KV heads (at most 1024)");
   if (layer < 0 || layer >= cache->num_layers) return fail(PKV_ERR_INVALID_ARG, "layer out of range");
   if (num_rows < 1 || total_q < 1) return fail(PKV_ERR_INVALID_ARG, "num_rows and total_q must be >= 1");
   if (!out || !q || !query_start || !block_tables || !context_lens)
@@ -594,7 +617,7 @@ extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t lay
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
        reinterpret_cast<uintptr_t>(cache->base)) & 15)
     return fail(PKV_ERR_INVALID_ARG, "out, q and cache->base must be 16-byte aligned");
-  const size_t need = pkv_prefill_workspace_size(cache, num_rows, total_q, max_q_per_row, max_context_len);
+  const size_t need = pkv_prefill_workspace_size_gqa(cache, num_q_heads, num_rows, total_q, max_q_per_row, max_context_len);
   if (!workspace || workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -607,7 +630,7 @@ extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t lay
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.max_splits = prefill_max_splits(max_context_len);
-  const size_t n = (size_t)total_q * cache->num_heads * a.max_splits;
+  const size_t n = (size_t)total_q * num_q_heads * a.max_splits;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + align256(n * kHeadDim * sizeof(float)));
   a.tok_splits = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(n * kHeadDim * sizeof(float)) +
@@ -616,6 +639,8 @@ extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t lay
   a.num_blocks = cache->num_blocks;
   a.num_layers = cache->num_layers;
   a.num_heads = cache->num_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = num_q_heads / cache->num_heads;
   a.bt_stride = bt_stride;
   a.num_rows = num_rows;
   a.total_q = total_q;
@@ -625,9 +650,9 @@ extern "C" int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t lay
   // with n == 1 add none, so ceil(total_q / kBQ) + num_rows bounds the count.
   const int64_t tiles = max_q_per_row >= 2 ? ((int64_t)total_q + kBQ - 1) / kBQ + num_rows : 0;
   const int64_t ranges = ((int64_t)max_context_len + kPrefillSplit - 1) / kPrefillSplit;
-  int64_t pre = tiles * ranges * cache->num_heads;
+  int64_t pre = tiles * ranges * num_q_heads;
   pre = (pre + kXcds - 1) / kXcds * kXcds;
-  const int head_groups = (cache->num_heads + kPrefillWaves - 1) / kPrefillWaves;
+  const int head_groups = (num_q_heads + kPrefillWaves - 1) / kPrefillWaves;
   int64_t dec = (int64_t)num_rows * decode_splits(max_context_len) * head_groups;
   dec = (dec + kXcds - 1) / kXcds * kXcds;
   if (pre + dec > INT32_MAX || tiles > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");

@@ -387,6 +387,40 @@ def pin_swap_roundtrip(seed=18):
                                       paged.decode(pool[:, l], q, tables, [29, 20], 0.25))
 
 
+def pin_grouped_query(seed=19):
+    """Grouped-query attention: with KV heads shared by groups of 4 query
+    heads, decode and prefill equal plain multi-head attention over a pool
+    whose every query head holds its own copy of KV head h // 4 (written with
+    the independent flat offsets), and brute force with that mapping spelled
+    out."""
+    rng = np.random.default_rng(seed)
+    Hkv, G, D, NB = 2, 4, 8, 12
+    Hq = Hkv * G
+    lens = [20, 5]
+    tables = np.array([[7, 3], [10, 0]], dtype=np.int32)
+    K = [_rand_bits(rng, (Hkv, L, D)) for L in lens]
+    V = [_rand_bits(rng, (Hkv, L, D)) for L in lens]
+    gqa = None
+    mha = None
+    for r, L in enumerate(lens):
+        a = _page_in_flat(NB, 1, Hkv, D, 0, tables[r], K[r], V[r])
+        dup = np.array([h // G for h in range(Hq)])
+        b = _page_in_flat(NB, 1, Hq, D, 0, tables[r], K[r][dup], V[r][dup])
+        gqa = a if gqa is None else np.where(np.isin(np.arange(NB), tables[r][:-(-L // 16)])[:, None, None, None, None, None], a, gqa)
+        mha = b if mha is None else np.where(np.isin(np.arange(NB), tables[r][:-(-L // 16)])[:, None, None, None, None, None], b, mha)
+    q = _rand_bits(rng, (2, Hq, D))
+    got = paged.decode(gqa[:, 0], q, tables, lens, 0.3, group=G)
+    np.testing.assert_array_equal(got, paged.decode(mha[:, 0], q, tables, lens, 0.3))
+    for r, L in enumerate(lens):
+        for h in range(Hq):
+            ref = brute.attend_one(_f64(q[r, h]).tolist(), _f64(K[r][h // G]).tolist(), _f64(V[r][h // G]).tolist(), 0.3)
+            np.testing.assert_allclose(got[r, h], ref, rtol=0, atol=1e-12)
+    qs = np.array([0, 3, 4])
+    qc = _rand_bits(rng, (4, Hq, D))
+    np.testing.assert_array_equal(paged.chunked_prefill(gqa[:, 0], qc, qs, tables, lens, 0.3, group=G),
+                                  paged.chunked_prefill(mha[:, 0], qc, qs, tables, lens, 0.3))
+
+
 ALL_PINS = [pin_block_arithmetic, pin_pool_capacity, pin_pool_semantics, pin_append_offsets,
             pin_gather_roundtrip, pin_bruteforce, pin_closed_forms, pin_decode_reads_own_token, pin_invariants,
-            pin_copy_on_write_divergence, pin_swap_roundtrip]
+            pin_copy_on_write_divergence, pin_swap_roundtrip, pin_grouped_query]

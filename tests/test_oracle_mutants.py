@@ -60,6 +60,12 @@ def _locate_swapped(row, position, block_size=16):
     return int(row[position % block_size if position % block_size < len(row) else 0]), position // block_size % block_size
 
 
+def _group_kv_tiled(K, V, group):
+    if group == 1:
+        return K, V
+    return np.tile(K, (group, 1, 1)), np.tile(V, (group, 1, 1))
+
+
 def _blocks_floor(n, block_size=16):
     return int(n) // block_size
 
@@ -72,6 +78,7 @@ MUTANTS = [
     ("gather_kv", _gather_reverse_slots),
     ("gather_kv", _gather_drop_tail),
     ("locate", _locate_swapped),
+    ("group_kv", _group_kv_tiled),
 ]
 
 
