@@ -331,6 +331,69 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
     }
 
 
+def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
+    """Decode step over an 8-bit cache: the average mix's 32 rows over a
+    32-layer, 7,152-block pool of FP8 E4M3 codes with one fp32 scale per
+    (token, head); per layer the 8-bit append of the 32 new tokens, then
+    decode.  Bytes = codes + scales of every cached token (8,448 B per token
+    and layer).  Codes are seeded random finite values: this leg times the
+    kernels; parity and the quality cost are checked by the tests."""
+    from workloads import SCALE
+
+    NB, NL, H = 7152, 32, 32
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4004)
+    codes = torch.empty((NB, NL, 2, H, 16, 128), dtype=torch.uint8, device=dev)
+    flat = codes.view(-1)
+    chunk = 1 << 30
+    for st in range(0, flat.numel(), chunk):
+        seg = flat[st:st + chunk]
+        seg.random_(0, 126, generator=gen)  # finite magnitudes; 0x7E = 448 is the largest
+        seg.bitwise_or_(torch.randint(0, 2, seg.shape, dtype=torch.uint8, device=dev, generator=gen) << 7)
+    scales = torch.empty((NB, NL, 2, H, 16), dtype=torch.float32, device=dev).uniform_(0.002, 0.006, generator=gen)
+    cache = pkv.PagedCache8(codes, scales)
+    R = batch.rows
+    tables = torch.from_numpy(batch.block_tables).to(dev)
+    lens = torch.from_numpy(batch.context_lens.astype(np.int32)).to(dev)
+    pos = torch.from_numpy((batch.context_lens - 1).astype(np.int32)).to(dev)
+    rot = torch.arange(R, dtype=torch.int32, device=dev)
+    maxL = int(batch.context_lens.max())
+    q = torch.from_numpy(batch.q.view(np.int16)).to(dev)
+    k = torch.from_numpy(batch.k_new.view(np.int16)).to(dev)
+    v = torch.from_numpy(batch.v_new.view(np.int16)).to(dev)
+    out = torch.empty((R, H, 128), dtype=torch.float16, device=dev)
+    ws = torch.empty(pkv.decode_workspace_size_fp8(cache, R, maxL), dtype=torch.uint8, device=dev)
+
+    def step():
+        for l in range(NL):
+            pkv.append_fp8(cache, l, k[l], v[l], pos, rot, tables, stream=stream)
+            pkv.decode_attention_fp8(cache, l, out, q[l], tables, lens, maxL, SCALE, ws, stream=stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tokens = float(batch.context_lens.sum())
+    nbytes = tokens * NL * 2 * H * (128 + 4)
+    del codes, scales, cache
+    return {
+        "workload": f"average-mix decode step over an 8-bit cache: {R} rows x {NL} layers, {H} heads x 128, FP8 E4M3 "
+                    f"codes + one fp32 scale per (token, head), {NB} blocks of 16 (append + decode per layer)",
+        "ms_per_step": ms,
+        "kv_tokens_per_s": tokens / (ms / 1e3),
+        "hbm_tb_s": nbytes / (ms / 1e3) / 1e12,
+        "hbm_frac_of_peak": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "vs_fp16_bytes": (128 + 4) / 256,
+    }
+
+
 def log(args, msg):
     if not args.quiet:
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -522,10 +585,12 @@ def main():
     blocks = None
     long_ctx = None
     gqa = None
+    fp8 = None
     if not args.no_extra:
         blocks = measure_block_copies(torch, pkv, cache, bp.free_list(), stream)
         long_ctx = measure_long_context(torch, pkv, cache, stream)
         gqa = measure_gqa(torch, pkv, batch, stream)
+        fp8 = measure_fp8(torch, pkv, batch, stream)
 
     prefill = None
     if not args.no_prefill:
@@ -566,6 +631,7 @@ def main():
         "trace": trace,
         "long_context": long_ctx,
         "gqa_decode": gqa,
+        "fp8_decode": fp8,
         "block_copy": blocks,
         "cpu_baseline": cpu_baseline,
     }

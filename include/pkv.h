@@ -299,6 +299,49 @@ int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids, const int32_
 int pkv_swap_out(const pkv_cache* cache, const int32_t* ids, int32_t n, void* host_dst, void* stream);
 int pkv_swap_in(const pkv_cache* cache, const void* host_src, const int32_t* ids, int32_t n, void* stream);
 
+/* ------------------------------------------------------------------------
+ * 8-bit KV cache.
+ *
+ * An 8-bit cache halves the bytes of every cached token and the attention
+ * read traffic, with a quality risk that grows with context length
+ * (Inference Infrastructure, seeitflow.com, "KV-cache precision"; The
+ * inference engine, wpnews.pro, "IO-aware attention and quantization attack
+ * different costs").  Codes are FP8 E4M3 (OCP format: bias 7, three mantissa
+ * bits, largest finite 448, 0x7F NaN) with one fp32 scale per (token, head)
+ * row of 128 values:
+ *   s = amax / 448, code = nearest E4M3 of x * (448 / amax) (ties to the even
+ *   mantissa, saturated at 448); a zero row has s = 0 and zero codes;
+ *   a cached value reads back as decode(code) * s.
+ *
+ * codes   device uint8 [num_blocks][num_layers][2][num_heads][16][128]
+ * scales  device fp32  [num_blocks][num_layers][2][num_heads][16]
+ * both 16-byte aligned and caller-owned; index 0 of the "2" axis is keys.
+ *
+ * pkv_append_fp8 takes FP16 k_new / v_new and places them exactly as
+ * pkv_append does (same arguments and contract); codes and scales are bit-
+ * exact with the definition above.  pkv_decode_attention_fp8 is
+ * pkv_decode_attention over the dequantized cache (same arguments, same
+ * split-K ranges and workspace size; fp32 arithmetic, FP16 output).
+ * ---------------------------------------------------------------------- */
+typedef struct pkv_cache8 {
+  void* codes;
+  void* scales;
+  int32_t num_blocks;
+  int32_t num_layers;
+  int32_t num_heads;
+  int32_t block_size;
+  int32_t head_dim;
+} pkv_cache8;
+
+int pkv_append_fp8(const pkv_cache8* cache, int32_t layer, const void* k_new, const void* v_new,
+                   const int32_t* positions, const int32_t* request_of_token, int32_t num_tokens,
+                   const int32_t* block_tables, int32_t num_rows, int32_t bt_stride, void* stream);
+size_t pkv_decode_workspace_size_fp8(const pkv_cache8* cache, int32_t num_rows, int32_t max_context_len);
+int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, void* out, const void* q,
+                             const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                             int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

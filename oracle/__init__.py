@@ -14,9 +14,11 @@ Contents
           inputs only.
   blocks  whole-block copies: copy-on-write inside the pool, swap out to and
           in from a host image.
+  fp8     the 8-bit cache: E4M3 codes with a scale per (token, head), append
+          and attention over the dequantized values.
 
 Pins (what holds this oracle to something other than itself) live in
 tests/test_oracle_*.py: the pages' printed block arithmetic, closed forms,
 invariants and the brute force.  No function here is "parity unpinned".
 """
-from . import blocks, brute, paged, pool  # noqa: F401
+from . import blocks, brute, fp8, paged, pool  # noqa: F401

@@ -262,3 +262,51 @@ def swap_in(cache: PagedCache, host_src, ids, stream=None):
     a = _i32(ids)
     buf = _host_buf(host_src, len(a) * block_bytes(cache), "host_src")
     _check(lib().pkv_swap_in(ctypes.byref(cache.desc), buf, _iptr(a), len(a), _stream_ptr(stream)))
+
+
+# ------------------------------------------------------------------ 8-bit cache
+
+class PagedCache8:
+    """Descriptor of a caller-owned 8-bit KV pool: codes [num_blocks, num_layers, 2,
+    num_heads, 16, 128] of uint8 (FP8 E4M3) and scales [num_blocks, num_layers, 2,
+    num_heads, 16] of float32, one per (token, head) row."""
+
+    def __init__(self, codes, scales):
+        if codes.dim() != 6 or codes.shape[2] != 2 or codes.shape[4] != BLOCK_SIZE or codes.shape[5] != HEAD_DIM:
+            raise ValueError("codes must be [num_blocks, num_layers, 2, num_heads, 16, 128]")
+        if tuple(scales.shape) != tuple(codes.shape[:5]):
+            raise ValueError("scales must be [num_blocks, num_layers, 2, num_heads, 16]")
+        _dptr(codes, "codes", 1)
+        _dptr(scales, "scales", 4)
+        self.codes, self.scales = codes, scales
+        nb, nl, _, nh, bs, hd = (int(x) for x in codes.shape)
+        self.desc = _lib.PkvCache8Desc(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                       nb, nl, nh, bs, hd)
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.desc.num_heads)
+
+
+def append_fp8(cache: PagedCache8, layer: int, k_new, v_new, positions, request_of_token, block_tables,
+               stream=None):
+    T = int(positions.numel())
+    R, stride = (int(x) for x in block_tables.shape)
+    _check(lib().pkv_append_fp8(ctypes.byref(cache.desc), int(layer), _dptr(k_new, "k_new", 2),
+                                _dptr(v_new, "v_new", 2), _dptr(positions, "positions", 4),
+                                _dptr(request_of_token, "request_of_token", 4), T,
+                                _dptr(block_tables, "block_tables", 4), R, stride, _stream_ptr(stream)))
+
+
+def decode_workspace_size_fp8(cache: PagedCache8, num_rows: int, max_context_len: int) -> int:
+    return int(lib().pkv_decode_workspace_size_fp8(ctypes.byref(cache.desc), int(num_rows), int(max_context_len)))
+
+
+def decode_attention_fp8(cache: PagedCache8, layer: int, out, q, block_tables, context_lens, max_context_len: int,
+                         scale: float, workspace=None, stream=None):
+    R, stride = (int(x) for x in block_tables.shape)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_decode_attention_fp8(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2),
+                                          _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,
+                                          _dptr(context_lens, "context_lens", 4), R, int(max_context_len),
+                                          float(scale), _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))

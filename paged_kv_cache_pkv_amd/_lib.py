@@ -20,6 +20,14 @@ class PkvCacheDesc(ctypes.Structure):
 
 PkvCacheDesc_p = ctypes.POINTER(PkvCacheDesc)
 
+
+class PkvCache8Desc(ctypes.Structure):
+    _fields_ = [("codes", c_vp), ("scales", c_vp), ("num_blocks", c_i32), ("num_layers", c_i32),
+                ("num_heads", c_i32), ("block_size", c_i32), ("head_dim", c_i32)]
+
+
+PkvCache8Desc_p = ctypes.POINTER(PkvCache8Desc)
+
 # name -> (restype, argtypes); mirrors include/pkv.h
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -52,6 +60,11 @@ SIGNATURES = {
     "pkv_chunked_prefill_attention_gqa": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32,
                                                          c_vp, c_i32, c_i32, c_i32, c_i32, ctypes.c_float, c_vp,
                                                          c_size, c_vp]),
+    "pkv_append_fp8": (ctypes.c_int, [PkvCache8Desc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                      c_vp]),
+    "pkv_decode_workspace_size_fp8": (c_size, [PkvCache8Desc_p, c_i32, c_i32]),
+    "pkv_decode_attention_fp8": (ctypes.c_int, [PkvCache8Desc_p, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                                ctypes.c_float, c_vp, c_size, c_vp]),
     "pkv_block_bytes": (c_size, [PkvCacheDesc_p]),
     "pkv_copy_blocks": (ctypes.c_int, [PkvCacheDesc_p, c_vp, c_vp, c_i32, c_vp]),
     "pkv_swap_out": (ctypes.c_int, [PkvCacheDesc_p, c_i32_p, c_i32, c_vp, c_vp]),

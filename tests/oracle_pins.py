@@ -23,6 +23,7 @@ import numpy as np
 
 import oracle.blocks as oblocks
 import oracle.brute as brute
+import oracle.fp8 as ofp8
 import oracle.paged as paged
 import oracle.pool as opool
 
@@ -421,6 +422,95 @@ def pin_grouped_query(seed=19):
                                   paged.chunked_prefill(mha[:, 0], qc, qs, tables, lens, 0.3))
 
 
+def pin_fp8_format(seed=20):
+    """E4M3 codes as the OCP 8-bit floating point format defines them (one sign,
+    four exponent bits with bias 7, three mantissa bits, no infinity, 0x7F NaN):
+    spot values, ties to the even mantissa, saturation at 448, and the encoder
+    against a brute-force nearest-code search."""
+    t = ofp8.decode_table()
+    for code, val in ((0x00, 0.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6), (0x38, 1.0), (0x3A, 1.25), (0x40, 2.0),
+                      (0x7E, 448.0), (0xC0, -2.0), (0x46, 3.5)):
+        assert t[code] == val, (hex(code), t[code], val)
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    enc = lambda x: int(ofp8.encode(np.float32(x)))
+    assert enc(1.0625) == 0x38 and enc(1.1875) == 0x3A      # halfway: to the even mantissa
+    assert enc(2.0 ** -10) == 0x00 and enc(3 * 2.0 ** -10) == 0x02  # subnormal ties
+    assert enc(1000.0) == 0x7E and enc(-1e6) == 0xFE and enc(464.0) == 0x7E  # saturation
+    finite = np.array([c for c in range(256) if not np.isnan(t[c])])
+    assert np.array_equal(ofp8.encode(t[finite].astype(np.float32)), finite.astype(np.uint8))
+    # brute force: the nearest finite code, ties to the even code
+    rng = np.random.default_rng(seed)
+    xs = np.concatenate([rng.uniform(-460, 460, 3000), rng.uniform(-0.03, 0.03, 3000),
+                         (t[finite][:-1] + t[finite][1:]) / 2]).astype(np.float32)
+    vals = t[finite]
+    for x in xs[:: 7]:
+        if abs(float(x)) >= 448.0:
+            continue
+        d = np.abs(vals - float(x))
+        best = np.flatnonzero(d == d.min())
+        cands = finite[best]
+        if len(cands) > 1:  # a tie between two neighbours: the one with the even mantissa
+            cands = [c for c in cands if (c & 1) == 0] or cands
+        want = {int(c) for c in cands}
+        # +0 / -0 both encode a zero
+        got = enc(x)
+        assert got in want or (t[got] == 0 and 0.0 in vals[best]), (float(x), hex(got), [hex(c) for c in want])
+
+
+def pin_fp8_quantized_cache(seed=21):
+    """Per-(token, head) quantization: every element within the format's
+    half-step of its value, each row's largest magnitude restored to fp32
+    rounding, zero rows kept, codes placed by the FP16 append's rule, and
+    decode over the cache equal to brute force over the dequantized values."""
+    rng = np.random.default_rng(seed)
+    H, D = 2, 128
+    x = _rand_bits(rng, (5, H, D))
+    x[2, 1] = 0  # a zero row
+    codes, sc = ofp8.quantize_rows(x)
+    xf = _f64(x)
+    deq = ofp8.dequantize(codes, sc)
+    bound = np.maximum(2.0 ** -4 * np.abs(xf), 2.0 ** -10 * sc[..., None] * 448.0 / 448.0 + 1e-12)
+    assert np.all(np.abs(deq - xf) <= bound * (1 + 1e-6))
+    amax = np.abs(xf).max(axis=-1)
+    rows = np.argmax(np.abs(xf), axis=-1)
+    got_max = np.take_along_axis(np.abs(deq), rows[..., None], axis=-1)[..., 0]
+    np.testing.assert_allclose(got_max, amax, rtol=2e-7, atol=0)
+    assert sc[2, 1] == 0 and not codes[2, 1].any()
+    # append places codes exactly where the FP16 append places values
+    NB, NL = 6, 2
+    cp = np.zeros((NB, NL, 2, H, 16, D), dtype=np.uint8)
+    sp = np.zeros((NB, NL, 2, H, 16), dtype=np.float32)
+    tables = np.array([[4, 1], [0, 5]], dtype=np.int32)
+    k, v = _rand_bits(rng, (3, H, D)), _rand_bits(rng, (3, H, D))
+    cp, sp = ofp8.append(cp, sp, 1, k, v, [17, 0, 31], [0, 1, 1], tables)
+    kc, ks = ofp8.quantize_rows(k)
+    for t, (r, pos) in enumerate(((0, 17), (1, 0), (1, 31))):
+        b, slot = int(tables[r, pos // 16]), pos % 16
+        assert np.array_equal(cp[b, 1, 0, :, slot], kc[t]) and np.array_equal(sp[b, 1, 0, :, slot], ks[t])
+    # decode over the cache: brute force over dequantized contiguous values
+    L = 20
+    ck = rng.integers(0, 0x7E, (H, L, D)).astype(np.uint8)
+    cv = rng.integers(0, 0x7E, (H, L, D)).astype(np.uint8) | (rng.integers(0, 2, (H, L, D)).astype(np.uint8) << 7)
+    sk = rng.uniform(0.001, 0.01, (H, L)).astype(np.float32)
+    sv = rng.uniform(0.001, 0.01, (H, L)).astype(np.float32)
+    pool_c = np.zeros((4, 1, 2, H, 16, D), dtype=np.uint8)
+    pool_s = np.zeros((4, 1, 2, H, 16), dtype=np.float32)
+    tab = np.array([[3, 0]], dtype=np.int32)
+    for j in range(L):
+        b, slot = int(tab[0, j // 16]), j % 16
+        pool_c[b, 0, 0, :, slot], pool_c[b, 0, 1, :, slot] = ck[:, j], cv[:, j]
+        pool_s[b, 0, 0, :, slot], pool_s[b, 0, 1, :, slot] = sk[:, j], sv[:, j]
+    q = _rand_bits(rng, (1, H, D))
+    got = ofp8.decode(pool_c, pool_s, 0, q, tab, [L], 0.25)
+    table = ofp8.decode_table()
+    for h in range(H):
+        Kd = [[table[ck[h, j, d]] * float(sk[h, j]) for d in range(D)] for j in range(L)]
+        Vd = [[table[cv[h, j, d]] * float(sv[h, j]) for d in range(D)] for j in range(L)]
+        ref = brute.attend_one(_f64(q[0, h]).tolist(), Kd, Vd, 0.25)
+        np.testing.assert_allclose(got[0, h], ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [pin_block_arithmetic, pin_pool_capacity, pin_pool_semantics, pin_append_offsets,
             pin_gather_roundtrip, pin_bruteforce, pin_closed_forms, pin_decode_reads_own_token, pin_invariants,
-            pin_copy_on_write_divergence, pin_swap_roundtrip, pin_grouped_query]
+            pin_copy_on_write_divergence, pin_swap_roundtrip, pin_grouped_query, pin_fp8_format,
+            pin_fp8_quantized_cache]

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import oracle.blocks as oblocks
+import oracle.fp8 as ofp8
 import oracle.paged as paged
 import oracle.pool as opool
 from tests import oracle_pins
@@ -124,6 +125,34 @@ def _swap_in_reversed(pool, host, ids):
                          ids=["copy_first_layer_only", "copy_wrong_direction", "swap_in_reversed"])
 def test_blocks_mutant_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(oblocks, name, fn)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {fn.__name__}"
+
+
+_encode = ofp8.encode
+_quantize_rows = ofp8.quantize_rows
+
+
+def _encode_round_half_up(x):
+    x = np.asarray(x, dtype=np.float32)
+    nudged = np.where(np.abs(x) > 0, x * np.float32(1 + 2.0 ** -20), x).astype(np.float32)
+    return _encode(nudged)
+
+
+def _quantize_wrong_scale(x_bits):
+    codes, sc = _quantize_rows(x_bits)
+    return codes, (sc * np.float32(448.0 / 447.0)).astype(np.float32)
+
+
+@pytest.mark.parametrize("name,fn", [("encode", _encode_round_half_up), ("quantize_rows", _quantize_wrong_scale)],
+                         ids=["encode_round_half_up", "quantize_wrong_scale"])
+def test_fp8_mutant_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(ofp8, name, fn)
     failed = []
     for pin in oracle_pins.ALL_PINS:
         try:
