@@ -380,8 +380,17 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the decode launch alone (decode + merge kernels), layers in turn
+    launches = 4 * NL
+    e0.record(stream)
+    for i in range(launches):
+        pkv.decode_attention_fp8(cache, i % NL, out, q[i % NL], tables, lens, maxL, SCALE, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = e0.elapsed_time(e1) / launches
     tokens = float(batch.context_lens.sum())
     nbytes = tokens * NL * 2 * H * (128 + 4)
+    layer_bytes = nbytes / NL
     del codes, scales, cache
     return {
         "workload": f"average-mix decode step over an 8-bit cache: {R} rows x {NL} layers, {H} heads x 128, FP8 E4M3 "
@@ -391,6 +400,9 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
         "hbm_tb_s": nbytes / (ms / 1e3) / 1e12,
         "hbm_frac_of_peak": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "vs_fp16_bytes": (128 + 4) / 256,
+        "decode_avg_launch_us": launch_ms * 1e3,
+        "decode_hbm_tb_s": layer_bytes / (launch_ms / 1e3) / 1e12,
+        "decode_frac_of_peak": layer_bytes / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
 
 

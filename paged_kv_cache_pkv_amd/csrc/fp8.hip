@@ -34,7 +34,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr int kRowCodes = kHeadDim;  // bytes of one (token, head) row
-constexpr int kF8Waves = 8;
+#ifndef PKV_F8_WAVES
+#define PKV_F8_WAVES 8
+#endif
+#ifndef PKV_F8_SPLIT_BLOCKS
+#define PKV_F8_SPLIT_BLOCKS 16
+#endif
+constexpr int kF8Waves = PKV_F8_WAVES;  // heads per workgroup, one wave each
+// Blocks per split-K range.  An 8-bit block moves half the bytes of an FP16
+// one, so a range may hold more blocks for the same fixed cost per range.
+constexpr int kF8SplitBlocks = PKV_F8_SPLIT_BLOCKS;
+static_assert(kF8SplitBlocks >= 1 && kF8SplitBlocks <= 64, "a range's block ids must fit one wave");
+__host__ __device__ constexpr int f8_splits(int L) {
+  return ((L + kBlockSize - 1) / kBlockSize + kF8SplitBlocks - 1) / kF8SplitBlocks;
+}
 constexpr int kF8Threads = 64 * kF8Waves;
 constexpr int kF8Xcds = 8;
 
@@ -153,25 +166,45 @@ __device__ __forceinline__ void codes8_to_f32(u32x2 w, float* out) {
   out[4] = c[0]; out[5] = c[1]; out[6] = d[0]; out[7] = d[1];
 }
 
-__device__ __forceinline__ void fold_f8(SoftmaxState& st, const F8Tile& t, const float* qf, float qk_scale, int group,
+// Dot product of eight FP16 query values with eight E4M3 codes.  Every E4M3
+// value is exact in FP16, so the codes are widened to packed halves (scale
+// exponent 0) and multiplied with the two-term FP16 dot, accumulating in fp32.
+__device__ __forceinline__ float dot8_f8(const uint4& q, u32x2 w) {
+  float acc = 0.0f;
+  acc = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.x), __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false), acc,
+                               false);
+  acc = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.y), __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true), acc,
+                               false);
+  acc = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.z), __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false), acc,
+                               false);
+  acc = __builtin_amdgcn_fdot2(bitcast<half2_t>(q.w), __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true), acc,
+                               false);
+  return acc;
+}
+
+// Fold one block (16 tokens; this lane's group holds tokens 4*group .. +3)
+// into the group's running softmax state.  Tail is set only for a block with
+// fewer than 16 live tokens (the row's last block, or an invalid id): its dead
+// tokens get score -inf and weight 0, and their codes are cleared, because
+// stale slots may hold NaN codes and scales (0 * NaN would leak).
+template <bool Tail>
+__device__ __forceinline__ void fold_f8(SoftmaxState& st, F8Tile& t, const uint4& q, float qk_scale, int group,
                                         int valid) {
   const float skv[4] = {t.sk.x, t.sk.y, t.sk.z, t.sk.w};
   const float svv[4] = {t.sv.x, t.sv.y, t.sv.z, t.sv.w};
   float s[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float k[8];
-    codes8_to_f32(t.k[i], k);
-    float acc = 0.0f;
+  for (int i = 0; i < 4; ++i) s[i] = sum16(dot8_f8(q, t.k[i])) * skv[i] * qk_scale;
+  bool live[4] = {true, true, true, true};
+  if (Tail) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(qf[e], k[e], acc);
-    s[i] = sum16(acc) * skv[i] * qk_scale;
-  }
-  bool live[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    live[i] = 4 * group + i < valid;
-    if (!live[i]) s[i] = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      live[i] = 4 * group + i < valid;
+      if (!live[i]) {
+        s[i] = -INFINITY;
+        t.v[i] = u32x2{0u, 0u};
+      }
+    }
   }
   const float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   const float mn = fmaxf(st.m, mb);
@@ -180,18 +213,12 @@ __device__ __forceinline__ void fold_f8(SoftmaxState& st, const F8Tile& t, const
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - mn);
   st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  float v[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    codes8_to_f32(t.v[i], v[i]);
-    if (!live[i]) {  // stale slots may hold NaN codes; 0 * NaN would leak
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
-    }
-  }
   float pw[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pw[i] = live[i] ? p[i] * svv[i] : 0.0f;
+  for (int i = 0; i < 4; ++i) pw[i] = (!Tail || live[i]) ? p[i] * svv[i] : 0.0f;
+  float v[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) codes8_to_f32(t.v[i], v[i]);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float acc = st.o[e] * alpha;
@@ -210,30 +237,29 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
   const int mq = n / kF8Xcds;
   const int hg = mq % head_groups;
   const int rs = (n % kF8Xcds) + kF8Xcds * (mq / head_groups);
+  const int h = __builtin_amdgcn_readfirstlane(hg * kF8Waves + (threadIdx.x >> 6));
+  if (h >= a.c.num_heads) return;
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
-  const int h = __builtin_amdgcn_readfirstlane(hg * kF8Waves + (threadIdx.x >> 6));
-  if (h >= a.c.num_heads) return;
+  int L = a.context_lens[r];
+  L = L > a.max_context_len ? a.max_context_len : L;
   const int lane = threadIdx.x & 63;
   const int group = lane >> 4;
   const int chunk = lane & 15;
-  int L = a.context_lens[r];
-  L = L > a.max_context_len ? a.max_context_len : L;
   const size_t rh = (size_t)r * a.c.num_heads + h;
   if (L < 1) {
     if (split == 0 && lane < 16) a.out[rh * 16 + lane] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
   const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const int nsplit = decode_splits(L);
+  const int nsplit = f8_splits(L);
   if (split >= nsplit) return;
-  const int b0 = split * kSplitBlocks;
-  const int b1 = min(nb, b0 + kSplitBlocks);
+  const int b0 = split * kF8SplitBlocks;
+  const int b1 = min(nb, b0 + kF8SplitBlocks);
   const int32_t* row_table = a.block_tables + (size_t)r * a.bt_stride;
   const int my_id = (lane < b1 - b0) ? row_table[b0 + lane] : 0;
-  float qf[8];
-  unpack8(a.q[rh * 16 + chunk], qf);
+  const uint4 q = a.q[rh * 16 + chunk];
   SoftmaxState st;
   st.m = kMinusBig;
   st.l = 0.0f;
@@ -258,7 +284,10 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
       if (jj + D - 1 < b1) issue(tile[(u + D - 1) % D], ok[(u + D - 1) % D], jj + D - 1);
       if (jj < b1) {
         const int valid = ok[u] ? min(L - jj * kBlockSize, kBlockSize) : 0;
-        fold_f8(st, tile[u], qf, a.qk_scale, group, valid);
+        if (valid == kBlockSize)
+          fold_f8<false>(st, tile[u], q, a.qk_scale, group, valid);
+        else
+          fold_f8<true>(st, tile[u], q, a.qk_scale, group, valid);
       }
     }
   }
@@ -291,7 +320,7 @@ __global__ __launch_bounds__(kF8Threads) void merge_fp8_kernel(F8Args a) {
   int L = a.context_lens[r];
   L = L > a.max_context_len ? a.max_context_len : L;
   if (L < 1) return;
-  const int nsplit = decode_splits(L);
+  const int nsplit = f8_splits(L);
   if (nsplit <= 1) return;
   const size_t rh = (size_t)r * a.c.num_heads + h;
   merge_partials(a.part_o + rh * a.max_splits * kHeadDim, a.part_ml + rh * a.max_splits, nsplit,
@@ -348,7 +377,7 @@ extern "C" int pkv_append_fp8(const pkv_cache8* cache, int32_t layer, const void
 extern "C" size_t pkv_decode_workspace_size_fp8(const pkv_cache8* cache, int32_t num_rows, int32_t max_context_len) {
   using namespace pkv;
   if (!cache || num_rows < 1 || max_context_len < 1 || cache->num_heads < 1) return 0;
-  const size_t s = (size_t)decode_splits(max_context_len);
+  const size_t s = (size_t)f8_splits(max_context_len);
   const size_t n = (size_t)num_rows * cache->num_heads * s;
   return align256(n * kHeadDim * sizeof(float)) + align256(n * sizeof(float2));
 }
@@ -368,7 +397,7 @@ extern "C" int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, 
   if (!(scale > 0.0f) || !__builtin_isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite and > 0");
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q)) & 15)
     return fail(PKV_ERR_INVALID_ARG, "out and q must be 16-byte aligned");
-  const int ms = decode_splits(max_context_len);
+  const int ms = f8_splits(max_context_len);
   const size_t need = pkv_decode_workspace_size_fp8(cache, num_rows, max_context_len);
   if (ms > 1) {
     if (!workspace || workspace_bytes < need)
