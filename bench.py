@@ -134,16 +134,11 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
     }
 
 
-def measure_trace(torch, steps=300, warm=5):
-    """Continuous-batching trace: up to 64 rows over a 36,864-block one-layer
-    pool, prompts U{50..8000}, answers U{1..1000}, a 2,000-token prefix
-    shared by reference counts; rows leave and are refilled every step.
-    The decode part of a step (grow, append one token per row, decode) is
-    timed with events separately from the fill of joining rows."""
+def _run_trace(torch, steps, warm, shared_decode):
     from paged_kv_cache_pkv_amd.trace import ContinuousBatchTrace
 
     tr = ContinuousBatchTrace(torch, seed=3, num_blocks=36864, max_rows=64, prefix_tokens=2000,
-                              prompt_range=(50, 8000), answer_range=(1, 1000))
+                              prompt_range=(50, 8000), answer_range=(1, 1000), shared_decode=shared_decode)
     for _ in range(warm):
         tr.step()
     torch.cuda.synchronize()
@@ -151,14 +146,33 @@ def measure_trace(torch, steps=300, warm=5):
     for _ in range(steps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         snap = tr.step(events=ev)
-        rec.append((ev, int(snap["lens"].sum()), len(snap["reqs"])))
+        sharers = sum(1 for r in tr.rows if r.shared)
+        rec.append((ev, int(snap["lens"].sum()), sharers))
     torch.cuda.synchronize()
     fill_ms = np.array([e[0].elapsed_time(e[1]) for e, _, _ in rec])
     step_ms = np.array([e[1].elapsed_time(e[2]) for e, _, _ in rec])
     tokens = np.array([t for _, t, _ in rec], dtype=np.float64)
+    sharers = np.array([n for _, _, n in rec], dtype=np.float64)
     joins = sum(1 for j in tr.log["joins"] if j[4] >= warm)
+    prefix = tr.prefix_tokens
     tr.drain()
     assert tr.pool.num_free == 36864, "trace leaked blocks"
+    return step_ms, fill_ms, tokens, sharers, joins, prefix
+
+
+def measure_trace(torch, steps=300, warm=5):
+    """Continuous-batching trace: up to 64 rows over a 36,864-block one-layer
+    pool, prompts U{50..8000}, answers U{1..1000}, a 2,000-token prefix
+    shared by reference counts; rows leave and are refilled every step.
+    The decode part of a step (grow, append one token per row, decode) is
+    timed with events separately from the fill of joining rows.  The same
+    seeded trace runs twice: with plain decode, and with the shared-prefix
+    decode that reads the prefix once per step for every 32 rows holding it."""
+    step_ms, fill_ms, tokens, sharers, joins, prefix = _run_trace(torch, steps, warm, False)
+    s_ms, _, s_tokens, s_sharers, _, _ = _run_trace(torch, steps, warm, True)
+    assert np.array_equal(tokens, s_tokens) and np.array_equal(sharers, s_sharers), "the two traces diverged"
+    # tokens the shared-prefix decode reads: the prefix once per tile of up to 32 sharing rows
+    physical = tokens - prefix * (sharers - np.ceil(sharers / 32.0))
     return {
         "workload": "continuous-batching trace: <=64 rows, one layer 32x128 FP16, 36,864-block pool, "
                     "prompts U{50..8000}, answers U{1..1000}, 2,000-token prefix shared by 125 ref-counted blocks",
@@ -172,6 +186,17 @@ def measure_trace(torch, steps=300, warm=5):
         "joins": joins,
         "fill_ms_total": float(fill_ms.sum()),
         "pool_drained": True,
+        "shared_prefix_decode": {
+            "decode_step_ms_p50": float(np.percentile(s_ms, 50)),
+            "decode_step_ms_p90": float(np.percentile(s_ms, 90)),
+            "decode_step_ms_max": float(s_ms.max()),
+            "sharing_rows_per_step_mean": float(sharers.mean()),
+            "read_kv_tokens_per_step_mean": float(physical.mean()),
+            "kv_tokens_per_s": float(tokens.sum() / (s_ms.sum() / 1e3)),
+            "logical_tb_s": float(tokens.sum() * LAYER_TOKEN_BYTES / (s_ms.sum() / 1e3) / 1e12),
+            "read_tb_s": float(physical.sum() * LAYER_TOKEN_BYTES / (s_ms.sum() / 1e3) / 1e12),
+            "speedup_vs_plain": float(step_ms.sum() / s_ms.sum()),
+        },
     }
 
 

@@ -259,6 +259,46 @@ int pkv_chunked_prefill_attention_gqa(const pkv_cache* cache, int32_t num_q_head
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Shared-prefix decode.
+ *
+ * Prefix blocks are computed once, held immutable and shared by reference
+ * count among every sequence whose prompt begins with them; in a multi-tenant
+ * step every concurrent sequence reads that one prefix (Build a continuous
+ * batching server, scalablesystem.dev, "Scaling and Performance"; Serving
+ * LLMs, "Prefix caching").  pkv_decode_attention_prefix computes exactly what
+ * pkv_decode_attention computes (every row attends over its own context), but
+ * reads the prefix once per step for all rows that share it: for each head
+ * and 256-token range of the prefix, the sharing rows' queries (32 at a time)
+ * form one matrix-core tile, and their partial softmax statistics merge with
+ * those of each row's own blocks.
+ *   shares_prefix  device int32 [num_rows]; nonzero marks a row whose first
+ *                  prefix_blocks table entries are the prefix's block ids
+ *                  (the same ids for every marked row: the prefix's ids are
+ *                  read from the first marked row's table).  A marked row
+ *                  with L <= 16 * prefix_blocks is decoded like an unmarked
+ *                  one.  May be NULL when prefix_blocks = 0.
+ *   prefix_blocks  host int, 0 <= P <= bt_stride; the prefix is P full
+ *                  blocks (16 P tokens).  P = 0 gives pkv_decode_attention's
+ *                  result bit for bit.
+ * Everything else is as in pkv_decode_attention (MHA: one query head per KV
+ * head).  Unmarked rows give the same bits as in pkv_decode_attention.  A
+ * marked row's ranges are the prefix's (16 blocks each, the last one possibly
+ * shorter) followed by 16-block ranges from block P on; they depend only on
+ * the row's length, its mark and P, so its output does not depend on the
+ * other rows of the batch.  Rows whose marks break the contract give
+ * unspecified output but no out-of-bounds access.
+ * The workspace needs pkv_decode_workspace_size_prefix(...) bytes, 256-byte
+ * aligned (it may be NULL when every row fits one range and P = 0).
+ * ---------------------------------------------------------------------- */
+size_t pkv_decode_workspace_size_prefix(const pkv_cache* cache, int32_t num_rows, int32_t max_context_len,
+                                        int32_t prefix_blocks);
+int pkv_decode_attention_prefix(const pkv_cache* cache, int32_t layer, void* out, const void* q,
+                                const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                                int32_t num_rows, int32_t max_context_len, float scale,
+                                const int32_t* shares_prefix, int32_t prefix_blocks, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole-block copies.
  *
  * A block with all its layers is one contiguous region of the pool of

@@ -192,6 +192,25 @@ def decode_attention_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q
                                           float(scale), _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
 
 
+def decode_workspace_size_prefix(cache: PagedCache, num_rows: int, max_context_len: int, prefix_blocks: int) -> int:
+    return int(lib().pkv_decode_workspace_size_prefix(ctypes.byref(cache.desc), int(num_rows), int(max_context_len),
+                                                      int(prefix_blocks)))
+
+
+def decode_attention_prefix(cache: PagedCache, layer: int, out, q, block_tables, context_lens, max_context_len: int,
+                            scale: float, shares_prefix, prefix_blocks: int, workspace=None, stream=None):
+    """Decode attention that reads a shared prefix of `prefix_blocks` blocks once
+    for every row marked in `shares_prefix` (device int32 [rows])."""
+    R, stride = (int(x) for x in block_tables.shape)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_decode_attention_prefix(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2),
+                                             _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,
+                                             _dptr(context_lens, "context_lens", 4), R, int(max_context_len),
+                                             float(scale), _dptr(shares_prefix, "shares_prefix", 4),
+                                             int(prefix_blocks), _dptr(workspace, "workspace"), ws_bytes,
+                                             _stream_ptr(stream)))
+
+
 def prefill_workspace_size(cache: PagedCache, num_rows: int, total_q: int, max_q_per_row: int,
                            max_context_len: int) -> int:
     return prefill_workspace_size_gqa(cache, cache.num_heads, num_rows, total_q, max_q_per_row, max_context_len)

@@ -53,6 +53,9 @@ SIGNATURES = {
     "pkv_chunked_prefill_attention": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
                                                      c_i32, c_i32, c_i32, c_i32, ctypes.c_float, c_vp, c_size,
                                                      c_vp]),
+    "pkv_decode_workspace_size_prefix": (c_size, [PkvCacheDesc_p, c_i32, c_i32, c_i32]),
+    "pkv_decode_attention_prefix": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                                   ctypes.c_float, c_vp, c_i32, c_vp, c_size, c_vp]),
     "pkv_decode_workspace_size_gqa": (c_size, [PkvCacheDesc_p, c_i32, c_i32, c_i32]),
     "pkv_decode_attention_gqa": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32,
                                                 c_i32, ctypes.c_float, c_vp, c_size, c_vp]),

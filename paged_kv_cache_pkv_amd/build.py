@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["errors.cpp", "pool.cpp", "append.hip", "decode.hip", "prefill.hip", "blocks.hip", "fp8.hip"]
+SOURCES = ["errors.cpp", "pool.cpp", "append.hip", "decode.hip", "prefill.hip", "blocks.hip", "fp8.hip", "prefix.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -23,7 +23,8 @@ import dataclasses
 
 import numpy as np
 
-from . import BLOCK_SIZE, BlockPool, PagedCache, append, decode_attention, decode_workspace_size
+from . import (BLOCK_SIZE, BlockPool, PagedCache, append, decode_attention, decode_attention_prefix,
+               decode_workspace_size, decode_workspace_size_prefix)
 
 
 def _seed(*parts: int) -> int:
@@ -51,7 +52,10 @@ class Row:
 class ContinuousBatchTrace:
     def __init__(self, torch, *, seed=3, num_blocks=36864, max_rows=64, prefix_tokens=2000,
                  prompt_range=(50, 8000), answer_range=(1, 1000), heads=32, stride=None, scale=None,
-                 device="cuda"):
+                 device="cuda", shared_decode=False):
+        # shared_decode: decode through pkv_decode_attention_prefix, which reads
+        # the shared prefix blocks once per step for every row holding them
+        self.shared_decode = shared_decode
         self.torch = torch
         self.seed = seed
         self.H = heads
@@ -77,7 +81,10 @@ class ContinuousBatchTrace:
         self.rows: list[Row] = []
         self.step_no = 0
         self.max_ctx = max_ctx
-        ws = decode_workspace_size(self.cache, max_rows, max_ctx)
+        if shared_decode:
+            ws = decode_workspace_size_prefix(self.cache, max_rows, max_ctx, self.prefix_tokens // BLOCK_SIZE)
+        else:
+            ws = decode_workspace_size(self.cache, max_rows, max_ctx)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
         self.log = {"prefix_ids": self.prefix_ids.copy(), "joins": [], "steps": []}
 
@@ -161,7 +168,12 @@ class ContinuousBatchTrace:
         lens_d = torch.from_numpy(lens).to(self.dev)
         out = torch.empty((R, self.H, 128), dtype=torch.float16, device=self.dev)
         append(self.cache, 0, k, v, pos_d, rot_d, tab_d)
-        decode_attention(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, self.ws)
+        if self.shared_decode:
+            marks = torch.from_numpy(np.array([1 if r.shared else 0 for r in self.rows], dtype=np.int32)).to(self.dev)
+            decode_attention_prefix(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, marks,
+                                    self.prefix_tokens // BLOCK_SIZE, self.ws)
+        else:
+            decode_attention(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, self.ws)
         if events:
             events[2].record()
         snap = {"step": self.step_no, "reqs": [r.req for r in self.rows], "lens": lens.copy(),

@@ -18,13 +18,14 @@ def _host_bits(t):
     return t.contiguous().cpu().view(__import__("torch").int16).numpy().view(np.uint16)
 
 
-def test_trace_parity_and_pool_invariants():
+@pytest.mark.parametrize("shared_decode", [False, True], ids=["plain-decode", "shared-prefix-decode"])
+def test_trace_parity_and_pool_invariants(shared_decode):
     torch = torch_cuda()
     from paged_kv_cache_pkv_amd.trace import ContinuousBatchTrace
 
     NB = 3000
     tr = ContinuousBatchTrace(torch, seed=11, num_blocks=NB, max_rows=8, prefix_tokens=512, prompt_range=(50, 1400),
-                              answer_range=(1, 40), heads=32)
+                              answer_range=(1, 40), heads=32, shared_decode=shared_decode)
     prefix = tr.prefix_ids.copy()
     npre = len(prefix)
     # the prefix blocks' contents as drawn, read back before any kernel runs
@@ -46,7 +47,7 @@ def test_trace_parity_and_pool_invariants():
         held = sum(r.nblk - r.shared // 16 for r in tr.rows)
         assert tr.pool.num_free + held + npre == NB
         if s % 7 == 3:
-            say(f"trace step {s}: rows {len(snap['reqs'])} lens {list(snap['lens'])}")
+            say(f"trace step {s} (shared_decode={shared_decode}): rows {len(snap['reqs'])} lens {list(snap['lens'])}")
             got = snap["out"].float().cpu().numpy()
             joins = {j[0]: j for j in tr.log["joins"]}
             for j, req in enumerate(snap["reqs"]):

@@ -204,6 +204,28 @@ def test_validation_append_args():
     assert L.pkv_append(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 16, None) == -1
 
 
+def test_validation_prefix_decode():
+    L = pkv.lib()
+    d = _desc()
+
+    def call(P, shares=FAKE, stride=16, maxL=256, ws=FAKE, wsb=1 << 20, **k):
+        return L.pkv_decode_attention_prefix(ctypes.byref(d), k.get("layer", 0), FAKE, FAKE, FAKE, stride, FAKE, 4,
+                                             maxL, 0.088, shares, P, ws, wsb, None)
+    assert call(-1) == -1
+    assert call(17) == -1            # more prefix blocks than table entries
+    assert call(3, shares=None) == -1
+    assert call(2, layer=1) == -1
+    # the workspace covers the prefix's ranges and a whole context's ranges
+    plain = L.pkv_decode_workspace_size(ctypes.byref(d), 4, 4096)
+    assert L.pkv_decode_workspace_size_prefix(ctypes.byref(d), 4, 4096, 0) == plain
+    need = L.pkv_decode_workspace_size_prefix(ctypes.byref(d), 4, 4096, 125)
+    per_range = 4 * 32 * (128 * 4 + 8)
+    assert need >= plain + 8 * per_range - 512
+    assert L.pkv_decode_workspace_size_prefix(ctypes.byref(d), 4, 4096, -1) == 0
+    assert call(125, stride=256, maxL=4096, wsb=need - 1) == -6
+    assert call(125, stride=256, maxL=4096, ws=None) == -6
+
+
 def test_validation_block_copies():
     L = pkv.lib()
     d = _desc(num_layers=3, num_heads=5)
