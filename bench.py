@@ -112,10 +112,50 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
 
+    def cold_chunk(batch, reps=10):
+        """The chunk with the 256 MB last-level cache scrubbed before every
+        launch (a 512 MB streaming write, outside the timed launch)."""
+        tables, qs, lens, q = d(batch.block_tables), d(batch.query_start), d(batch.context_lens), d(batch.q[0])
+        T, maxq, maxL = batch.total_q, int(batch.q_counts.max()), int(batch.context_lens.max())
+        ws = torch.empty(pkv.prefill_workspace_size(cache, batch.rows, T, maxq, maxL), dtype=torch.uint8, device=dev)
+        out = torch.empty((T, 32, 128), dtype=torch.float16, device=dev)
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ms = []
+        for _ in range(reps):
+            scrub.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.chunked_prefill_attention(cache, 0, out, q, qs, tables, lens, maxq, maxL, SCALE, ws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        del scrub
+        return float(np.median(ms))
+
+    def bulk_append(tokens, reps=20):
+        """Append a whole prompt's K/V (one row, positions 0..tokens-1)."""
+        b = build_batch(f"append{tokens}", 11, [tokens], [tokens], num_blocks=7152, with_pool=False)
+        tables, pos, rot = d(b.block_tables), d(b.positions), d(b.request_of_token)
+        k, v = d(b.k_new[0]), d(b.v_new[0])
+        pkv.append(cache, 0, k, v, pos, rot, tables, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pkv.append(cache, 0, k, v, pos, rot, tables, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = tokens * 2 * LAYER_TOKEN_BYTES / (ms / 1e3) / 1e9  # each K/V byte read once, written once
+        return {"tokens": tokens, "us": ms * 1e3, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS}
+
     mixed = c5_mixed(with_pool=False)
     chunk = build_batch("chunk-only", 4, [8000], [512], num_blocks=7152, with_pool=False, stride=520)
     app_mixed_ms, mixed_ms = timed(mixed)
     _, chunk_ms = timed(chunk)
+    chunk_cold_ms = cold_chunk(chunk)
+    appends = [bulk_append(n) for n in (512, 8000)]
     flops = prefill_flops(chunk)
     kv_mixed = float(mixed.context_lens.sum()) * LAYER_TOKEN_BYTES
     tflops = flops / (chunk_ms / 1e3) / 1e12
@@ -127,7 +167,9 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
         "mixed_hbm_gb_s": kv_mixed / (mixed_ms / 1e3) / 1e9,
         "chunk_only_launch_us": chunk_ms * 1e3,
         "chunk_flops": flops,
+        "chunk_only_cold_cache_us": chunk_cold_ms * 1e3,
         "append_543_tokens_us": app_mixed_ms * 1e3,
+        "append_bulk_roofline": appends,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
                      "kernel": "pkv_chunked_prefill_attention on the chunk alone (tile + merge launches)"},
@@ -263,6 +305,43 @@ def measure_block_copies(torch, pkv, cache, free_ids, stream, n=64, reps=10):
         "swap_in_gb_s": moved / (in_ms / 1e3) / 1e9,
         "swap_note": "device <-> pinned host over the host link, one DMA copy per run of consecutive ids",
     }
+
+
+def measure_tiny(torch, pkv, dev, stream, reps=50):
+    """The tiny decode configuration (4 rows with contexts 17/40/100/256, one
+    layer, 64-block pool): append + decode per step.  Its 6.8 MB stay in the
+    caches, so this is the path's launch latency, not a bandwidth figure."""
+    from workloads import SCALE, c1_tiny
+
+    b = c1_tiny(seed=0)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    pool = d(b.pool)
+    cache = pkv.PagedCache(pool)
+    tables, lens, pos, rot = d(b.block_tables), d(b.context_lens), d(b.positions), d(b.request_of_token)
+    q, k, v = d(b.q[0]), d(b.k_new[0]), d(b.v_new[0])
+    maxL = int(b.context_lens.max())
+    ws = torch.empty(pkv.decode_workspace_size(cache, b.rows, maxL), dtype=torch.uint8, device=dev)
+    out = torch.empty((b.rows, 32, 128), dtype=torch.float16, device=dev)
+
+    def step():
+        pkv.append(cache, 0, k, v, pos, rot, tables, stream=stream)
+        pkv.decode_attention(cache, 0, out, q, tables, lens, maxL, SCALE, ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"workload": "4 rows, contexts 17/40/100/256, one layer, 64-block pool: append + decode",
+            "us_per_step": ms * 1e3, "kv_tokens": int(b.context_lens.sum())}
 
 
 def measure_long_context(torch, pkv, cache, stream, steps=5, warm=2):
@@ -556,10 +635,13 @@ def main():
     tokens = 0
     t_start.record(stream)
     wall0 = time.perf_counter()
+    step_ev = events(args.steps + 1)
     for i, k in enumerate(range(args.warmup, total_steps)):
         step_tokens = host_step(k)
         tokens += step_tokens
+        step_ev[i].record(stream)
         gpu_step(i)
+    step_ev[args.steps].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -574,6 +656,7 @@ def main():
     traffic = counted_traffic()
 
     ms_per_step = elapsed_ms / args.steps
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
     value = tokens / (elapsed_ms / 1e3)
 
     # ---------------- CPU baseline leg: the oracle as it stands, timed on a bounded sample
@@ -623,11 +706,13 @@ def main():
     long_ctx = None
     gqa = None
     fp8 = None
+    tiny = None
     if not args.no_extra:
         blocks = measure_block_copies(torch, pkv, cache, bp.free_list(), stream)
         long_ctx = measure_long_context(torch, pkv, cache, stream)
         gqa = measure_gqa(torch, pkv, batch, stream)
         fp8 = measure_fp8(torch, pkv, batch, stream)
+        tiny = measure_tiny(torch, pkv, dev, stream)
 
     prefill = None
     if not args.no_prefill:
@@ -645,6 +730,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -670,6 +756,7 @@ def main():
         "gqa_decode": gqa,
         "fp8_decode": fp8,
         "block_copy": blocks,
+        "tiny_decode": tiny,
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(rec), flush=True)

@@ -29,3 +29,22 @@ def host_f64(t):
 
 def say(msg):
     print(msg, flush=True)
+
+
+def ramp_keys(b, top=8.0):
+    """Scale each row's key at position p by 1 + (top - 1) * p / L, in the pool
+    and in the step's new tokens alike, so that scores keep growing along the
+    context and a running softmax maximum moves again and again.  Rows must
+    not share blocks."""
+    pool = b.pool.view(np.float16).copy()
+    k_new = b.k_new.view(np.float16).copy()
+    for r in range(b.rows):
+        L, n = int(b.context_lens[r]), int(b.q_counts[r])
+        first_new = L - n
+        for p in range(first_new):
+            pool[b.block_tables[r, p // 16], :, 0, :, p % 16, :] *= np.float16(1 + (top - 1) * p / L)
+        for i in range(n):
+            k_new[:, b.query_start[r] + i] *= np.float16(1 + (top - 1) * (first_new + i) / L)
+    b.pool = pool.view(np.uint16)
+    b.k_new = k_new.view(np.uint16)
+    return b

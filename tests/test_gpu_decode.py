@@ -7,7 +7,7 @@ import pytest
 
 import oracle.paged as opaged
 import paged_kv_cache_pkv_amd as pkv
-from tests.gpu_util import dev, host_f64, say, torch_cuda
+from tests.gpu_util import dev, host_f64, ramp_keys, say, torch_cuda
 from tests.tolerance import assert_close
 from workloads import SCALE, build_batch, c1_tiny
 
@@ -150,3 +150,16 @@ def test_poisoned_slots_do_not_leak():
     got, _ = gpu_decode(b, torch)
     assert np.isfinite(got).all()
     assert_close(got, oracle_decode(b), "poison")
+
+
+def test_decode_growing_scores():
+    """Keys grow along the context (up to 8x), so every range's running maximum
+    keeps moving and old partial sums are rescaled many times."""
+    torch = torch_cuda()
+    lens = [300, 1100, 2600, 40]
+    b = ramp_keys(build_batch("ramp", 51, lens, np.ones(len(lens)), num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                              stride=max(-(-L // 16) for L in lens) + 2))
+    say(f"decode growing scores lens={lens}")
+    got, _ = gpu_decode(b, torch)
+    s = assert_close(got, oracle_decode(b), "growing scores")
+    say(f"  {s}")

@@ -5,7 +5,7 @@ import pytest
 
 import oracle.paged as opaged
 import paged_kv_cache_pkv_amd as pkv
-from tests.gpu_util import dev, say, torch_cuda
+from tests.gpu_util import dev, ramp_keys, say, torch_cuda
 from tests.tolerance import assert_close
 from workloads import SCALE, build_batch, c5_mixed
 
@@ -134,3 +134,16 @@ def test_split_chunk_matches_one_call():
     assert_close(g1, got[:192], "first half")
     ref = oracle_prefill(b)
     assert_close(got, ref, "one call")
+
+
+def test_prefill_growing_scores():
+    """Keys grow along the context (up to 8x): a chunk's exponent reference must
+    move inside a key range, and a decode row's running maximum with it."""
+    torch = torch_cuda()
+    lens, qc = [2600, 900, 3000], [300, 1, 2]
+    b = ramp_keys(build_batch("ramp", 52, lens, qc, num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                              stride=max(-(-L // 16) for L in lens) + 2))
+    say(f"prefill growing scores lens={lens} q={qc}")
+    got, _ = gpu_prefill(b, torch)
+    s = assert_close(got, oracle_prefill(b), "growing scores")
+    say(f"  {s}")
