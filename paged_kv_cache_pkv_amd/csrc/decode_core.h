@@ -105,6 +105,86 @@ __device__ __forceinline__ void fold_tile(SoftmaxState* st, KVTile& t, const uin
     }
 }
 
+// The same fold for G >= 2 query heads per KV head, where the vector work per
+// byte grows with G.  Two changes keep it small:
+//  - the exponent reference m moves only when a block's maximum passes it by
+//    more than kGroupLazy (log2 units), so the common block rescales nothing
+//    and its weights stay below 2^kGroupLazy;
+//  - the weights are rounded to FP16 and P*V runs as v_dot2_f32_f16 over
+//    pairs of tokens (one FP16 pair of values per dim), half the
+//    instructions of fp32 multiply-adds on unpacked values.  The row sum adds
+//    the same rounded weights, so numerator and denominator agree.
+constexpr float kGroupLazy = 8.0f;
+
+template <int G>
+__device__ __forceinline__ void fold_tile_group(SoftmaxState* st, KVTile& t, const uint4* q, float qk_scale, int group,
+                                                int valid) {
+  float s[G][4];  // raw dot products; the scale is applied with the reference
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[g][i] = sum16(dot8(q[g], t.k[i]));
+  if (valid < kBlockSize) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (group + 4 * i >= valid) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[g][i] = -INFINITY;
+        t.v[i] = make_uint4(0u, 0u, 0u, 0u);  // stale slots may hold NaN; 0 * NaN would leak
+      }
+    }
+  }
+  float mb[G];
+  bool move = false;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    mb[g] = fmaxf(fmaxf(s[g][0], s[g][1]), fmaxf(s[g][2], s[g][3])) * qk_scale;
+    move = move || mb[g] > st[g].m + kGroupLazy;
+  }
+  if (__any(move)) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(st[g].m, mb[g]);
+      const float alpha = fast_exp2(st[g].m - mn);
+      st[g].l *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st[g].o[e] *= alpha;
+      st[g].m = mn;
+    }
+  }
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  half2_t p01[G], p23[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    p01[g].x = (_Float16)fast_exp2(fmaf(s[g][0], qk_scale, -st[g].m));
+    p01[g].y = (_Float16)fast_exp2(fmaf(s[g][1], qk_scale, -st[g].m));
+    p23[g].x = (_Float16)fast_exp2(fmaf(s[g][2], qk_scale, -st[g].m));
+    p23[g].y = (_Float16)fast_exp2(fmaf(s[g][3], qk_scale, -st[g].m));
+    st[g].l = __builtin_amdgcn_fdot2(p23[g], ones, __builtin_amdgcn_fdot2(p01[g], ones, st[g].l, false), false);
+  }
+  // values as FP16 pairs (token 4i, token 4i + 1 of this lane's stripe) per dim
+  half2_t v01[8], v23[8];
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&t.v[0]);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&t.v[1]);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&t.v[2]);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&t.v[3]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const half2_t a = bitcast<half2_t>(w0[w]), b = bitcast<half2_t>(w1[w]);
+    const half2_t c = bitcast<half2_t>(w2[w]), d = bitcast<half2_t>(w3[w]);
+    v01[2 * w] = half2_t{a.x, b.x};
+    v01[2 * w + 1] = half2_t{a.y, b.y};
+    v23[2 * w] = half2_t{c.x, d.x};
+    v23[2 * w + 1] = half2_t{c.y, d.y};
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      st[g].o[e] = __builtin_amdgcn_fdot2(p23[g], v23[e], __builtin_amdgcn_fdot2(p01[g], v01[e], st[g].o[e], false),
+                                          false);
+}
+
 // Merge the four 16-lane groups' states; every lane ends with the same bits.
 __device__ __forceinline__ void merge_groups(SoftmaxState& st) {
   float M = fmaxf(st.m, shfl_xor(st.m, 16));
@@ -177,7 +257,10 @@ __device__ __forceinline__ void fold_blocks(const uint16_t* __restrict__ pool, i
       if (jj + kAhead < b1) issue(tile[(u + kAhead) % Depth], ok[(u + kAhead) % Depth], jj + kAhead);
       if (jj < b1) {
         const int valid = ok[u] ? min(L - jj * kBlockSize, kBlockSize) : 0;
-        fold_tile<G>(st, tile[u], q, qk_scale, group, valid);
+        if constexpr (G == 1)
+          fold_tile<1>(st, tile[u], q, qk_scale, group, valid);
+        else
+          fold_tile_group<G>(st, tile[u], q, qk_scale, group, valid);
       }
     }
   }

@@ -7,7 +7,7 @@ import pytest
 
 import oracle.paged as opaged
 import paged_kv_cache_pkv_amd as pkv
-from tests.gpu_util import dev, host_bits, host_f64, say, torch_cuda
+from tests.gpu_util import dev, host_bits, host_f64, ramp_keys, say, torch_cuda
 from tests.tolerance import assert_close
 from workloads import SCALE, build_batch
 
@@ -62,6 +62,24 @@ def test_gqa_decode_parity(G):
         got = _decode(torch, pool, Hq, layer, q, b.block_tables, b.context_lens)
         ref = opaged.decode(pool[:, layer], q, b.block_tables, b.context_lens, SCALE, group=G)
         assert_close(host_f64(got), ref, f"G={G} layer {layer}")
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_gqa_decode_growing_scores(G):
+    """Keys grow along the context (up to 8x), so the grouped fold's deferred
+    exponent reference moves again and again inside a range."""
+    torch = torch_cuda()
+    Hkv = 8 if G < 8 else 4
+    Hq = Hkv * G
+    lens = [300, 1100, 2600, 40]
+    b = ramp_keys(build_batch(f"gqa-ramp-G{G}", 60 + G, lens, [1] * len(lens),
+                              num_blocks=sum(-(-L // 16) for L in lens) + 8, num_heads=Hkv, stride=170))
+    q = _queries(70 + G, len(lens), Hq)
+    pool = _full_pool(b)
+    say(f"gqa decode growing scores G={G}")
+    got = _decode(torch, pool, Hq, 0, q, b.block_tables, b.context_lens)
+    ref = opaged.decode(pool[:, 0], q, b.block_tables, b.context_lens, SCALE, group=G)
+    assert_close(host_f64(got), ref, f"growing scores G={G}")
 
 
 @pytest.mark.parametrize("G", [2, 4, 8])
