@@ -24,23 +24,39 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const int32_t* __restrict__ request_of_token, const int32_t* __restrict__ block_tables, int num_rows,
     int bt_stride) {
   const int t = blockIdx.x;
-  const int r = request_of_token[t];
-  const int p = positions[t];
-  if (r < 0 || r >= num_rows || p < 0 || (p >> 4) >= bt_stride) return;
-  const int b = block_tables[(size_t)r * bt_stride + (p >> 4)];
-  if (b < 0 || b >= num_blocks) return;
-  const int slot = p & 15;
   const int chunks = num_heads * (kHeadDim / 8);  // 16-byte chunks per K (or V) of one token
-  const size_t k_slab = slab_offset(b, layer, 0, 0, num_layers, num_heads);
-  const size_t v_slab = slab_offset(b, layer, 1, 0, num_layers, num_heads);
-  for (int c = threadIdx.x; c < 2 * chunks; c += kAppendThreads) {
-    const bool is_v = c >= chunks;
-    const int rem = is_v ? c - chunks : c;
-    const int h = rem >> 4;
-    const int part = rem & 15;
-    const uint4 val = (is_v ? v_new : k_new)[(size_t)t * chunks + rem];
-    const size_t dst = (is_v ? v_slab : k_slab) + (size_t)h * (kBlockSize * kHeadDim) + slot * kHeadDim + part * 8;
-    *reinterpret_cast<uint4*>(pool + dst) = val;
+  // The token's data does not depend on where it goes: its loads are issued
+  // first, so that they overlap the dependent reads of the row, the position
+  // and the block id.
+  constexpr int kPer = 4;  // chunks per lane in flight
+  for (int c0 = 0; c0 < 2 * chunks; c0 += kPer * kAppendThreads) {
+    uint4 val[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = c0 + u * kAppendThreads + threadIdx.x;
+      const bool is_v = c >= chunks;
+      val[u] = c < 2 * chunks ? (is_v ? v_new : k_new)[(size_t)t * chunks + (is_v ? c - chunks : c)]
+                             : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int r = request_of_token[t];
+    const int p = positions[t];
+    if (r < 0 || r >= num_rows || p < 0 || (p >> 4) >= bt_stride) return;
+    const int b = block_tables[(size_t)r * bt_stride + (p >> 4)];
+    if (b < 0 || b >= num_blocks) return;
+    const int slot = p & 15;
+    const size_t k_slab = slab_offset(b, layer, 0, 0, num_layers, num_heads);
+    const size_t v_slab = slab_offset(b, layer, 1, 0, num_layers, num_heads);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = c0 + u * kAppendThreads + threadIdx.x;
+      if (c >= 2 * chunks) continue;
+      const bool is_v = c >= chunks;
+      const int rem = is_v ? c - chunks : c;
+      const int h = rem >> 4;
+      const int part = rem & 15;
+      const size_t dst = (is_v ? v_slab : k_slab) + (size_t)h * (kBlockSize * kHeadDim) + slot * kHeadDim + part * 8;
+      *reinterpret_cast<uint4*>(pool + dst) = val[u];
+    }
   }
 }
 

@@ -84,44 +84,54 @@ __device__ __forceinline__ uint32_t encode_e4m3(float x) {
 // One workgroup per new token; 16 lanes per (kv, head) row, 8 values each.
 constexpr int kAppendThreads = 256;
 
+// Maximum over each aligned group of 16 lanes (one DPP row); every lane of
+// the group receives it.
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // lane ^ 1
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // lane ^ 2
+  v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+  return v;
+}
+
+// One workgroup per (new token, 16 of its 2 * num_heads K/V rows): 16 lanes
+// per row take 8 values each.  Every (token, row) is independent, so all of a
+// step's rows run at once rather than in passes behind each other's loads.
 __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(
     Cache8 c, int layer, const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
     const int32_t* __restrict__ positions, const int32_t* __restrict__ request_of_token,
     const int32_t* __restrict__ block_tables, int num_rows, int bt_stride) {
   const int t = blockIdx.x;
+  const int row = blockIdx.y * (kAppendThreads / 16) + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  const int rows = 2 * c.num_heads;
+  if (row >= rows) return;  // whole 16-lane groups leave together
+  const int kv = row / c.num_heads;
+  const int h = row % c.num_heads;
+  // the token's values first: their load overlaps the dependent reads of the
+  // row, the position and the block id
+  const uint4 raw = (kv ? v_new : k_new)[((size_t)t * c.num_heads + h) * 16 + part];
   const int r = request_of_token[t];
   const int p = positions[t];
   if (r < 0 || r >= num_rows || p < 0 || (p >> 4) >= bt_stride) return;
   const int b = block_tables[(size_t)r * bt_stride + (p >> 4)];
   if (b < 0 || b >= c.num_blocks) return;
   const int slot = p & 15;
-  const int part = threadIdx.x & 15;
-  const int rows = 2 * c.num_heads;
-  // every lane of a 16-lane group runs the same number of passes (rows is uniform)
-  for (int row = threadIdx.x >> 4; row < ((rows + 15) / 16) * 16; row += kAppendThreads / 16) {
-    const bool live = row < rows;
-    const int kv = live ? row / c.num_heads : 0;
-    const int h = live ? row % c.num_heads : 0;
-    const uint4 raw = live ? (kv ? v_new : k_new)[((size_t)t * c.num_heads + h) * 16 + part] : make_uint4(0u, 0u, 0u, 0u);
-    float x[8];
-    unpack8(raw, x);
-    float amax = 0.0f;
+  float x[8];
+  unpack8(raw, x);
+  float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = max16(amax);
+  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+  uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, shfl_xor(amax, off));
-    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-    uint32_t lo = 0, hi = 0;
+  for (int e = 0; e < 4; ++e) lo |= (amax > 0.0f ? encode_e4m3(x[e] * inv) : 0u) << (8 * e);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) lo |= (amax > 0.0f ? encode_e4m3(x[e] * inv) : 0u) << (8 * e);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) hi |= (amax > 0.0f ? encode_e4m3(x[4 + e] * inv) : 0u) << (8 * e);
-    if (live) {
-      const size_t ri = row_index(b, layer, kv, h, slot, c.num_layers, c.num_heads);
-      *reinterpret_cast<uint2*>(c.codes + ri * kRowCodes + part * 8) = make_uint2(lo, hi);
-      if (part == 0) c.scales[ri] = amax > 0.0f ? amax / 448.0f : 0.0f;
-    }
-  }
+  for (int e = 0; e < 4; ++e) hi |= (amax > 0.0f ? encode_e4m3(x[4 + e] * inv) : 0u) << (8 * e);
+  const size_t ri = row_index(b, layer, kv, h, slot, c.num_layers, c.num_heads);
+  *reinterpret_cast<uint2*>(c.codes + ri * kRowCodes + part * 8) = make_uint2(lo, hi);
+  if (part == 0) c.scales[ri] = amax > 0.0f ? amax / 448.0f : 0.0f;
 }
 
 struct F8Tile {
@@ -368,7 +378,8 @@ extern "C" int pkv_append_fp8(const pkv_cache8* cache, int32_t layer, const void
   if (num_rows < 1 || bt_stride < 1) return fail(PKV_ERR_INVALID_ARG, "num_rows and bt_stride must be >= 1");
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
     return fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
-  append_fp8_kernel<<<dim3(num_tokens), dim3(kAppendThreads), 0, static_cast<hipStream_t>(stream)>>>(
+  const unsigned row_groups = (unsigned)((2 * cache->num_heads + kAppendThreads / 16 - 1) / (kAppendThreads / 16));
+  append_fp8_kernel<<<dim3(num_tokens, row_groups), dim3(kAppendThreads), 0, static_cast<hipStream_t>(stream)>>>(
       cache8_of(cache), layer, static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), positions,
       request_of_token, block_tables, num_rows, bt_stride);
   return check_launch("pkv_append_fp8");
