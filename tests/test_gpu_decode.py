@@ -56,6 +56,8 @@ CASES = [
     ("multi-split", 32, 2, [513, 1000, 1024, 1025, 1537, 2047, 2600]),
     ("odd-heads", 5, 1, [1, 600, 3, 1300]),
     ("one-head-long", 1, 1, [4100, 8192]),
+    # more than 64 ranges per row: the merge takes its ranges in several passes of 64
+    ("beyond-64-ranges", 2, 1, [20000, 16400, 16385, 7]),
 ]
 
 

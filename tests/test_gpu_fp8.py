@@ -85,6 +85,25 @@ def test_decode_fp8_parity(name, layers, lens):
         assert_close(host_f64(out), ref, f"{name} layer {layer}")
 
 
+def test_decode_fp8_beyond_64_ranges():
+    """Rows of 79 and 65 ranges: the 8-bit merge takes its ranges in several passes of 64."""
+    torch = torch_cuda()
+    lens = [20000, 16400, 300]
+    b = build_batch("fp8-long", 33, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 4,
+                    num_layers=1, num_heads=2, stride=max(-(-L // 16) for L in lens))
+    pool = opaged.append(b.pool, 0, b.k_new[0], b.v_new[0], b.positions, b.request_of_token, b.block_tables)
+    codes, scales = _quantized_pool(pool)
+    cache, _, _ = _gpu_cache(torch, codes, scales)
+    ws = torch.empty(pkv.decode_workspace_size_fp8(cache, len(lens), max(lens)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((len(lens), 2, 128), dtype=torch.float16, device="cuda")
+    say(f"decode fp8 beyond 64 ranges lens={lens}")
+    pkv.decode_attention_fp8(cache, 0, out, dev(b.q[0], torch), dev(b.block_tables, torch),
+                             dev(b.context_lens, torch), max(lens), SCALE, ws)
+    torch.cuda.synchronize()
+    ref = ofp8.decode(codes, scales, 0, b.q[0], b.block_tables, b.context_lens, SCALE)
+    assert_close(host_f64(out), ref, "fp8 beyond 64 ranges")
+
+
 def test_fp8_append_then_decode():
     """End to end: the library quantizes the step's tokens, then decode reads
     them (each row attends over its own new token)."""

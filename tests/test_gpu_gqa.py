@@ -64,6 +64,22 @@ def test_gqa_decode_parity(G):
         assert_close(host_f64(got), ref, f"G={G} layer {layer}")
 
 
+def test_gqa_decode_beyond_64_ranges():
+    """Grouped decode (G = 4) over rows of 79 and 65 ranges: the merge takes its
+    ranges in several passes of 64."""
+    torch = torch_cuda()
+    G, Hkv = 4, 2
+    lens = [20000, 16400, 90]
+    b = build_batch("gqa-long", 44, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 4,
+                    num_heads=Hkv, stride=max(-(-L // 16) for L in lens))
+    q = _queries(45, len(lens), Hkv * G)
+    pool = _full_pool(b)
+    say(f"gqa decode beyond 64 ranges lens={lens}")
+    got = _decode(torch, pool, Hkv * G, 0, q, b.block_tables, b.context_lens)
+    ref = opaged.decode(pool[:, 0], q, b.block_tables, b.context_lens, SCALE, group=G)
+    assert_close(host_f64(got), ref, "gqa beyond 64 ranges")
+
+
 @pytest.mark.parametrize("G", [4, 8])
 def test_gqa_decode_growing_scores(G):
     """Keys grow along the context (up to 8x), so the grouped fold's deferred

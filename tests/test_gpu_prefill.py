@@ -44,6 +44,8 @@ CASES = [
     ("tile-edges", 32, [129, 130, 256, 2, 1000], [128, 129, 256, 2, 1]),
     ("ranges", 8, [5000, 2100, 4100], [200, 2100, 64]),
     ("odd-heads", 5, [900, 33, 2049], [257, 1, 3]),
+    # a decode row of 67 ranges and a chunk of 9 prefill ranges, merged in the same call
+    ("long-rows", 2, [17000, 18200, 600], [1, 140, 300]),
 ]
 
 
