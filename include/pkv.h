@@ -19,6 +19,8 @@
  *  - Return value: PKV_OK (0) or a negative PKV_ERR_* code.  On error nothing
  *    has been launched or changed, and pkv_last_error() (thread-local) holds a
  *    message.  Scalar arguments are validated on the host before any launch.
+ *    The one exception is PKV_ERR_HIP from a call that queues several
+ *    launches or copies: what was queued before the refused one stays queued.
  *  - Device pointers are owned by the caller and must stay valid until the
  *    work queued on `stream` has finished.  The library never allocates or
  *    frees device memory and never synchronizes the stream.
@@ -194,7 +196,7 @@ int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void* out, const
 int32_t pkv_split_tokens(void);
 
 /* ------------------------------------------------------------------------
- * Chunked-prefill attention mixed with decode rows in one launch.
+ * Chunked-prefill attention mixed with decode rows in one call.
  *
  * Row r owns queries q[query_start[r] .. query_start[r+1]) (device FP16
  * [total_q][num_heads][128]); they are the last n_r = query_start[r+1] -
@@ -237,8 +239,8 @@ int pkv_chunked_prefill_attention(const pkv_cache* cache, int32_t layer, void* o
  * [rows or tokens][num_q_heads][128]; everything else is as in
  * pkv_decode_attention / pkv_chunked_prefill_attention, which are these calls
  * with num_q_heads = num_heads.
- *   decode: G in {1, 2, 4, 8}, else PKV_ERR_UNSUPPORTED.  One wave reads a KV
- *           head's keys and values once for all G query heads.
+ *   decode: G in {1, 2, 4, 8}, else PKV_ERR_UNSUPPORTED.  Each key and value
+ *           of a KV head is read once for all G query heads of its group.
  *   prefill: any G with num_q_heads <= 1024.  Each query head's tile reads
  *           its group's K/V tile (from cache when the group's tiles run
  *           together); decode rows of the launch likewise.
