@@ -538,7 +538,8 @@ def main():
     batch = c2_average_mix(seed=args.seed, with_pool=False)
     R = batch.rows
     stride = batch.bt_stride
-    total_steps = args.warmup + args.steps
+    UNFUSED_STEPS = 5  # after the timed steps: the same step with the append as its own launch
+    total_steps = args.warmup + args.steps + UNFUSED_STEPS
     lens0 = batch.context_lens.astype(np.int64)
     max_ctx = int(lens0.max()) + total_steps
     if -(-max_ctx // 16) > stride:
@@ -607,14 +608,23 @@ def main():
     def sampled_layers(i):
         return {(2 * i) % NL, (2 * i + NL // 2) % NL}
 
-    def gpu_step(i):
+    def gpu_step(i, fused=True):
+        """Per layer: the step's append and decode attention.  By default one
+        fused call (the range holding each row's new token appends it);
+        fused=False runs pkv_append then pkv_decode_attention."""
         pick = sampled_layers(i) if i is not None else ()
         for l in range(NL):
-            pkv.append(cache, l, k_d[l], v_d[l], pos_d, rot_d, tables_d, stream=stream)
+            if not fused:
+                pkv.append(cache, l, k_d[l], v_d[l], pos_d, rot_d, tables_d, stream=stream)
             if l in pick:
                 e0, e1 = spare_events.pop(), spare_events.pop()
                 e0.record(stream)
-            pkv.decode_attention(cache, l, out_d[l], q_d[l], tables_d, lens_d, max_ctx, SCALE, ws_d, stream=stream)
+            if fused:
+                pkv.decode_attention_append(cache, l, out_d[l], q_d[l], k_d[l], v_d[l], tables_d, lens_d, max_ctx,
+                                            SCALE, ws_d, stream=stream)
+            else:
+                pkv.decode_attention(cache, l, out_d[l], q_d[l], tables_d, lens_d, max_ctx, SCALE, ws_d,
+                                     stream=stream)
             if l in pick:
                 e1.record(stream)
                 samples.append((i, l, e0, e1))
@@ -636,7 +646,7 @@ def main():
     t_start.record(stream)
     wall0 = time.perf_counter()
     step_ev = events(args.steps + 1)
-    for i, k in enumerate(range(args.warmup, total_steps)):
+    for i, k in enumerate(range(args.warmup, args.warmup + args.steps)):
         step_tokens = host_step(k)
         tokens += step_tokens
         step_ev[i].record(stream)
@@ -647,6 +657,17 @@ def main():
     wall = time.perf_counter() - wall0
     elapsed_ms = t_start.elapsed_time(t_end)
     log(args, f"timed {args.steps} steps: {elapsed_ms:.2f} ms (wall {wall * 1e3:.1f} ms)")
+
+    # the same step with pkv_append as a launch of its own, for comparison (not the headline)
+    u0, u1 = events(2)
+    unfused_tokens = 0
+    u0.record(stream)
+    for k in range(args.warmup + args.steps, total_steps):
+        unfused_tokens += host_step(k)
+        gpu_step(None, fused=False)
+    u1.record(stream)
+    torch.cuda.synchronize()
+    unfused_ms = u0.elapsed_time(u1) / UNFUSED_STEPS
 
     dec_ms = [e0.elapsed_time(e1) for (_, _, e0, e1) in samples]
     dec_avg_ms = float(np.mean(dec_ms))
@@ -731,6 +752,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "step_path": "per layer one pkv_decode_attention_append call (append fused into decode)",
+        "unfused_step": {"ms_per_step": unfused_ms,
+                         "kv_tokens_per_s": unfused_tokens / (unfused_ms * UNFUSED_STEPS / 1e3),
+                         "path": "per layer pkv_append then pkv_decode_attention", "steps": UNFUSED_STEPS},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -745,7 +770,7 @@ def main():
         "hbm_frac_of_peak": value * STEP_TOKEN_BYTES / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "pkv_decode_attention (split + merge launches), one layer",
+                     "kernel": "pkv_decode_attention_append (split + merge launches, the append fused), one layer",
                      "avg_launch_ms": dec_avg_ms, "bytes_per_launch": bytes_per_decode,
                      "launches_timed": len(dec_ms)},
         "wall_s_timed": wall,

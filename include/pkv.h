@@ -195,6 +195,23 @@ int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void* out, const
 /* Tokens per split-K range of the decode kernel. */
 int32_t pkv_split_tokens(void);
 
+/* Decode with the step's append fused in.  Row r's new token sits at position
+ * context_lens[r] - 1, and its keys and values are k_new[r] and v_new[r]
+ * (device FP16 [num_rows][num_heads][128], 16-byte aligned).  The call writes
+ * them into their slot, exactly as pkv_append with positions[r] =
+ * context_lens[r] - 1 and request_of_token[r] = r.  It then returns
+ * pkv_decode_attention's result: the same bits, in the pool and in out, as
+ * those two calls in sequence.  The range that holds a row's last token takes
+ * that token from k_new / v_new, so the step needs one launch fewer
+ * (faangrind scheduler step 7: each decode row appends its token, then
+ * attends).  Same contract and workspace as pkv_decode_attention; the
+ * appended slot must not be in a shared block.  Rows with context_lens[r] < 1
+ * append nothing. */
+int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer, void* out, const void* q, const void* k_new,
+                                const void* v_new, const int32_t* block_tables, int32_t bt_stride,
+                                const int32_t* context_lens, int32_t num_rows, int32_t max_context_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Chunked-prefill attention mixed with decode rows in one call.
  *

@@ -52,12 +52,17 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* part_o;        // [R][Hq][S][128]
   float2* part_ml;      // [R][Hq][S]
+  const uint4* k_new;   // [R][H][16]: this step's new token per row (appending decode only)
+  const uint4* v_new;
   int layer, num_blocks, num_layers, num_heads;  // num_heads: KV heads of the pool
   int num_q_heads;      // num_heads * G
   int bt_stride, num_rows, max_context_len, max_splits;
   float qk_scale;       // scale * log2(e)
 };
 
+// kAppend: each row's new token (position L - 1) comes from k_new / v_new and
+// the range holding it also writes it into its pool slot (the step's append).
+template <bool kAppend>
 __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_kernel(DecodeArgs a) {
   // 1-D grid over (row, range, head group).  Workgroups go to the XCDs
   // round-robin by index; with the remap, the head groups of one (row,
@@ -89,8 +94,14 @@ __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_ke
   }
   if (split >= decode_splits(L)) return;
   const size_t slot = rh * a.max_splits + split;
-  decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h, a.block_tables + (size_t)r * a.bt_stride,
-               L, split, a.q + rh * 16, a.qk_scale, a.out + rh * 16, a.part_o + slot * kHeadDim, a.part_ml + slot);
+  if constexpr (kAppend)
+    decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
+                 a.block_tables + (size_t)r * a.bt_stride, L, split, a.q + rh * 16, a.qk_scale, a.out + rh * 16,
+                 a.part_o + slot * kHeadDim, a.part_ml + slot, a.k_new + rh * 16, a.v_new + rh * 16);
+  else
+    decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
+                 a.block_tables + (size_t)r * a.bt_stride, L, split, a.q + rh * 16, a.qk_scale, a.out + rh * 16,
+                 a.part_o + slot * kHeadDim, a.part_ml + slot);
 }
 
 // Grouped-query decode: G query heads share each KV head.  A workgroup of
@@ -243,11 +254,13 @@ extern "C" int pkv_decode_attention(const pkv_cache* cache, int32_t layer, void*
                                   num_rows, max_context_len, scale, workspace, workspace_bytes, stream);
 }
 
-extern "C" int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,
-                                        const void* q, const int32_t* block_tables, int32_t bt_stride,
-                                        const int32_t* context_lens, int32_t num_rows, int32_t max_context_len,
-                                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace pkv;
+namespace pkv {
+namespace {
+
+int decode_launch(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out, const void* q,
+                  const void* k_new, const void* v_new, const int32_t* block_tables, int32_t bt_stride,
+                  const int32_t* context_lens, int32_t num_rows, int32_t max_context_len, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc = check_cache(cache)) return rc;
   const int G = group_of(cache, num_q_heads);
   if (!G) return fail(PKV_ERR_UNSUPPORTED, "num_q_heads must be 1, 2, 4 or 8 times the pool's KV heads");
@@ -278,6 +291,8 @@ extern "C" int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_he
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = workspace ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + align256(n * kHeadDim * sizeof(float)))
                         : nullptr;
+  a.k_new = static_cast<const uint4*>(k_new);
+  a.v_new = static_cast<const uint4*>(v_new);
   a.layer = layer;
   a.num_blocks = cache->num_blocks;
   a.num_layers = cache->num_layers;
@@ -297,7 +312,10 @@ extern "C" int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_he
     const int head_groups = (cache->num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
     const int64_t wgs = rs_total * head_groups;
     if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-    decode_split_kernel<<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
+    if (k_new)
+      decode_split_kernel<true><<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
+    else
+      decode_split_kernel<false><<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
   } else {
     const int64_t wgs = rs_total * cache->num_heads;
     if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
@@ -314,4 +332,29 @@ extern "C" int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_he
     if (int rc = check_launch("decode merge kernel")) return rc;
   }
   return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,
+                                        const void* q, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* context_lens, int32_t num_rows, int32_t max_context_len,
+                                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return pkv::decode_launch(cache, num_q_heads, layer, out, q, nullptr, nullptr, block_tables, bt_stride, context_lens,
+                            num_rows, max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer, void* out, const void* q,
+                                           const void* k_new, const void* v_new, const int32_t* block_tables,
+                                           int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
+                                           int32_t max_context_len, float scale, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  using namespace pkv;
+  if (!cache) return fail(PKV_ERR_INVALID_ARG, "cache is null");
+  if (!k_new || !v_new) return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  return decode_launch(cache, cache->num_heads, layer, out, q, k_new, v_new, block_tables, bt_stride, context_lens,
+                       num_rows, max_context_len, scale, workspace, workspace_bytes, stream);
 }

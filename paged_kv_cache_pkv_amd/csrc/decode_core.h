@@ -210,14 +210,28 @@ __device__ __forceinline__ void merge_groups(SoftmaxState& st) {
 // 16 chunks apart).  Depth = blocks whose loads are in flight per wave (plus
 // the one being folded); the fold order, and so the result, does not depend
 // on it.
+//
+// With new_k non-null, the context's last token (position L - 1, in block
+// b1 - 1) is this step's new token: its keys and values come from new_k /
+// new_v (16 chunks of this KV head) rather than from the pool, and the wave
+// also writes them into their pool slot -- the append of that token for this
+// head.  The bits folded are the ones an append followed by this fold would
+// read back, so the result is the same.
 template <int Depth, int G>
 __device__ __forceinline__ void fold_blocks(const uint16_t* __restrict__ pool, int layer, int num_blocks,
                                             int num_layers, int num_kv_heads, int h_kv,
                                             const int32_t* __restrict__ row_table, int L, int b0, int b1,
-                                            const uint4* __restrict__ q_head, float qk_scale, SoftmaxState* st) {
+                                            const uint4* __restrict__ q_head, float qk_scale, SoftmaxState* st,
+                                            const uint4* __restrict__ new_k = nullptr,
+                                            const uint4* __restrict__ new_v = nullptr) {
   const int lane = threadIdx.x & 63;
   const int group = lane >> 4;  // token within each 4-token stripe
   const int chunk = lane & 15;  // dims 8*chunk .. 8*chunk+7
+  uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;
+  if (new_k) {
+    nk = new_k[chunk];
+    nv = new_v[chunk];
+  }
 
   // One vector load brings the blocks' ids; readlane hands them out.
   const int my_id = (lane < b1 - b0) ? row_table[b0 + lane] : 0;
@@ -257,6 +271,24 @@ __device__ __forceinline__ void fold_blocks(const uint16_t* __restrict__ pool, i
       if (jj + kAhead < b1) issue(tile[(u + kAhead) % Depth], ok[(u + kAhead) % Depth], jj + kAhead);
       if (jj < b1) {
         const int valid = ok[u] ? min(L - jj * kBlockSize, kBlockSize) : 0;
+        if (new_k && jj == b1 - 1 && ok[u]) {
+          // slot s of the last block holds the new token: lanes of group s % 4,
+          // stripe entry s / 4
+          const int s = (L - 1) & (kBlockSize - 1);
+          const bool mine = group == (s & 3);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (mine && i == (s >> 2)) {
+              tile[u].k[i] = nk;
+              tile[u].v[i] = nv;
+            }
+          if (mine) {
+            const int id = __builtin_amdgcn_readlane(my_id, jj - b0);
+            uint16_t* slot_k = const_cast<uint16_t*>(head_base) + (size_t)id * block_stride + s * kHeadDim + chunk * 8;
+            *reinterpret_cast<uint4*>(slot_k) = nk;
+            *reinterpret_cast<uint4*>(reinterpret_cast<char*>(slot_k) + vdelta) = nv;
+          }
+        }
         if constexpr (G == 1)
           fold_tile<1>(st, tile[u], q, qk_scale, group, valid);
         else
@@ -279,7 +311,8 @@ __device__ __forceinline__ void decode_range(const uint16_t* __restrict__ pool, 
                                              const int32_t* __restrict__ row_table, int L, int split,
                                              const uint4* __restrict__ q_head, float qk_scale,
                                              uint4* __restrict__ out_head, float* __restrict__ part_o,
-                                             float2* __restrict__ part_ml) {
+                                             float2* __restrict__ part_ml, const uint4* __restrict__ new_k = nullptr,
+                                             const uint4* __restrict__ new_v = nullptr) {
   const int lane = threadIdx.x & 63;
   const int chunk = lane & 15;
   const int nb = (L + kBlockSize - 1) / kBlockSize;
@@ -287,7 +320,10 @@ __device__ __forceinline__ void decode_range(const uint16_t* __restrict__ pool, 
   const int b0 = split * kSplitBlocks;
   const int b1 = min(nb, b0 + kSplitBlocks);
   SoftmaxState st;
-  fold_blocks<Depth, 1>(pool, layer, num_blocks, num_layers, num_heads, h, row_table, L, b0, b1, q_head, qk_scale, &st);
+  // only the range holding the last token takes the new one
+  const bool last = split == nsplit - 1;
+  fold_blocks<Depth, 1>(pool, layer, num_blocks, num_layers, num_heads, h, row_table, L, b0, b1, q_head, qk_scale, &st,
+                        last ? new_k : nullptr, last ? new_v : nullptr);
   if (nsplit == 1) {
     if (lane < 16) {
       const float inv = 1.0f / st.l;
