@@ -422,10 +422,28 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the same step with each row's new token appended in the decode launch
+    kn = torch.from_numpy(rng.standard_normal((R, kv_heads, 128), dtype=np.float32).astype(np.float16)).to(dev)
+    vn = torch.from_numpy(rng.standard_normal((R, kv_heads, 128), dtype=np.float32).astype(np.float16)).to(dev)
+
+    def step_append():
+        for l in range(NL):
+            pkv.decode_attention_append_gqa(cache, q_heads, l, out, q[l], kn, vn, tables, lens, maxL, SCALE, ws,
+                                            stream=stream)
+
+    step_append()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step_append()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_append = e0.elapsed_time(e1) / steps
     tokens = float(batch.context_lens.sum())
     kv_bytes = tokens * NL * 2 * kv_heads * 128 * 2
     del pool
     return {
+        "ms_per_step_with_fused_append": ms_append,
         "workload": f"average-mix decode with grouped-query attention: {R} rows x {NL} layers, {kv_heads} KV heads, "
                     f"{q_heads} query heads, FP16, {NB} blocks of 16",
         "ms_per_step": ms,

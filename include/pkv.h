@@ -269,6 +269,14 @@ int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_
                              const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
                              int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
                              size_t workspace_bytes, void* stream);
+/* pkv_decode_attention_append with G query heads per KV head: k_new / v_new
+ * are [num_rows][num_heads][128] (the pool's KV heads), q and out
+ * [num_rows][num_q_heads][128]. */
+int pkv_decode_attention_append_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                                    int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 size_t pkv_prefill_workspace_size_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t num_rows,
                                       int32_t total_q, int32_t max_q_per_row, int32_t max_context_len);
 int pkv_chunked_prefill_attention_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,

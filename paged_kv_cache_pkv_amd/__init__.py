@@ -195,14 +195,20 @@ def decode_attention_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q
 def decode_attention_append(cache: PagedCache, layer: int, out, q, k_new, v_new, block_tables, context_lens,
                             max_context_len: int, scale: float, workspace=None, stream=None):
     """Append each row's new token at position context_lens[r] - 1, then decode (one fused launch)."""
+    decode_attention_append_gqa(cache, cache.num_heads, layer, out, q, k_new, v_new, block_tables, context_lens,
+                                max_context_len, scale, workspace, stream)
+
+
+def decode_attention_append_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q, k_new, v_new, block_tables,
+                                context_lens, max_context_len: int, scale: float, workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_decode_attention_append(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2),
-                                             _dptr(q, "q", 2), _dptr(k_new, "k_new", 2), _dptr(v_new, "v_new", 2),
-                                             _dptr(block_tables, "block_tables", 4), stride,
-                                             _dptr(context_lens, "context_lens", 4), R, int(max_context_len),
-                                             float(scale), _dptr(workspace, "workspace"), ws_bytes,
-                                             _stream_ptr(stream)))
+    _check(lib().pkv_decode_attention_append_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(layer),
+                                                 _dptr(out, "out", 2), _dptr(q, "q", 2), _dptr(k_new, "k_new", 2),
+                                                 _dptr(v_new, "v_new", 2), _dptr(block_tables, "block_tables", 4),
+                                                 stride, _dptr(context_lens, "context_lens", 4), R,
+                                                 int(max_context_len), float(scale), _dptr(workspace, "workspace"),
+                                                 ws_bytes, _stream_ptr(stream)))
 
 
 def decode_workspace_size_prefix(cache: PagedCache, num_rows: int, max_context_len: int, prefix_blocks: int) -> int:

@@ -51,6 +51,9 @@ SIGNATURES = {
     "pkv_split_tokens": (c_i32, []),
     "pkv_decode_attention_append": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
                                                    c_i32, c_i32, ctypes.c_float, c_vp, c_size, c_vp]),
+    "pkv_decode_attention_append_gqa": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                       c_i32, c_vp, c_i32, c_i32, ctypes.c_float, c_vp, c_size,
+                                                       c_vp]),
     "pkv_prefill_workspace_size": (c_size, [PkvCacheDesc_p, c_i32, c_i32, c_i32, c_i32]),
     "pkv_chunked_prefill_attention": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
                                                      c_i32, c_i32, c_i32, c_i32, ctypes.c_float, c_vp, c_size,

@@ -121,7 +121,7 @@ constexpr int kGqaWaves = PKV_GQA_WAVES;
 constexpr int kGqaThreads = 64 * kGqaWaves;
 static_assert(kSplitBlocks % kGqaWaves == 0, "each wave takes an equal share of a range");
 
-template <int G>
+template <int G, bool kAppend>
 __global__ __launch_bounds__(kGqaThreads) void decode_gqa_kernel(DecodeArgs a) {
   __shared__ float s_m[kGqaWaves][G], s_l[kGqaWaves][G];
   __shared__ float4 s_o[kGqaWaves][G][32];
@@ -156,9 +156,18 @@ __global__ __launch_bounds__(kGqaThreads) void decode_gqa_kernel(DecodeArgs a) {
   const int b0 = min(nb, split * kSplitBlocks + wave * kPer);
   const int b1 = min(nb, b0 + kPer);
   SoftmaxState st[G];
+  // with the append fused, the wave holding the row's last block takes the new token
+  const uint4* new_k = nullptr;
+  const uint4* new_v = nullptr;
+  if constexpr (kAppend) {
+    if (b0 < b1 && b1 == nb) {
+      new_k = a.k_new + ((size_t)r * a.num_heads + h) * 16;
+      new_v = a.v_new + ((size_t)r * a.num_heads + h) * 16;
+    }
+  }
   fold_blocks<(G >= 8 ? 2 : PKV_GQA_DEPTH), G>(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
                                         a.block_tables + (size_t)r * a.bt_stride, L, b0, b1, a.q + rh * 16,
-                                        a.qk_scale, st);
+                                        a.qk_scale, st, new_k, new_v);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (lane < 16) {
@@ -319,10 +328,19 @@ int decode_launch(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, vo
   } else {
     const int64_t wgs = rs_total * cache->num_heads;
     if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-    switch (G) {
-      case 2: decode_gqa_kernel<2><<<dim3((unsigned)wgs), dim3(kGqaThreads), 0, s>>>(a); break;
-      case 4: decode_gqa_kernel<4><<<dim3((unsigned)wgs), dim3(kGqaThreads), 0, s>>>(a); break;
-      default: decode_gqa_kernel<8><<<dim3((unsigned)wgs), dim3(kGqaThreads), 0, s>>>(a); break;
+    const dim3 grid((unsigned)wgs), block(kGqaThreads);
+    if (k_new) {
+      switch (G) {
+        case 2: decode_gqa_kernel<2, true><<<grid, block, 0, s>>>(a); break;
+        case 4: decode_gqa_kernel<4, true><<<grid, block, 0, s>>>(a); break;
+        default: decode_gqa_kernel<8, true><<<grid, block, 0, s>>>(a); break;
+      }
+    } else {
+      switch (G) {
+        case 2: decode_gqa_kernel<2, false><<<grid, block, 0, s>>>(a); break;
+        case 4: decode_gqa_kernel<4, false><<<grid, block, 0, s>>>(a); break;
+        default: decode_gqa_kernel<8, false><<<grid, block, 0, s>>>(a); break;
+      }
     }
   }
   if (int rc = check_launch("decode split kernel")) return rc;
@@ -345,16 +363,27 @@ extern "C" int pkv_decode_attention_gqa(const pkv_cache* cache, int32_t num_q_he
                             num_rows, max_context_len, scale, workspace, workspace_bytes, stream);
 }
 
-extern "C" int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer, void* out, const void* q,
-                                           const void* k_new, const void* v_new, const int32_t* block_tables,
-                                           int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
-                                           int32_t max_context_len, float scale, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
+extern "C" int pkv_decode_attention_append_gqa(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, void* out,
+                                               const void* q, const void* k_new, const void* v_new,
+                                               const int32_t* block_tables, int32_t bt_stride,
+                                               const int32_t* context_lens, int32_t num_rows, int32_t max_context_len,
+                                               float scale, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pkv;
   if (!cache) return fail(PKV_ERR_INVALID_ARG, "cache is null");
   if (!k_new || !v_new) return fail(PKV_ERR_INVALID_ARG, "null device pointer");
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
     return fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
-  return decode_launch(cache, cache->num_heads, layer, out, q, k_new, v_new, block_tables, bt_stride, context_lens,
+  return decode_launch(cache, num_q_heads, layer, out, q, k_new, v_new, block_tables, bt_stride, context_lens,
                        num_rows, max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer, void* out, const void* q,
+                                           const void* k_new, const void* v_new, const int32_t* block_tables,
+                                           int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
+                                           int32_t max_context_len, float scale, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (!cache) return pkv::fail(PKV_ERR_INVALID_ARG, "cache is null");
+  return pkv_decode_attention_append_gqa(cache, cache->num_heads, layer, out, q, k_new, v_new, block_tables, bt_stride,
+                                         context_lens, num_rows, max_context_len, scale, workspace, workspace_bytes,
+                                         stream);
 }

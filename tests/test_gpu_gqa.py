@@ -147,3 +147,39 @@ def test_gqa_prefill_parity_and_duplicated_heads(G):
     assert_close(host_f64(got), ref, f"prefill G={G}")
     want = _prefill(torch, _duplicate_heads(pool, G), Hq, q, b)
     assert np.array_equal(host_bits(got), host_bits(want))
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_gqa_appending_decode_equals_append_then_decode_bitwise(G):
+    """pkv_decode_attention_append_gqa leaves the same pool bytes and output
+    bits as pkv_append followed by pkv_decode_attention_gqa."""
+    torch = torch_cuda()
+    Hkv = 8 if G < 8 else 4
+    Hq = Hkv * G
+    lens = [1, 16, 17, 63, 64, 65, 257, 700, 2600]
+    b = build_batch(f"gqa-fused-G{G}", 80 + G, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 6,
+                    num_layers=2, num_heads=Hkv, stride=max(-(-L // 16) for L in lens) + 2)
+    q = _queries(90 + G, len(lens), Hq)
+    layer = 1
+    R, maxL = len(lens), max(lens)
+    say(f"gqa appending decode G={G} vs append + decode")
+
+    def run(fused):
+        pool_d = dev(b.pool, torch)
+        cache = pkv.PagedCache(pool_d)
+        ws = torch.empty(pkv.decode_workspace_size_gqa(cache, Hq, R, maxL), dtype=torch.uint8, device="cuda")
+        out = torch.empty((R, Hq, 128), dtype=torch.float16, device="cuda")
+        tables, lens_d = dev(b.block_tables, torch), dev(b.context_lens, torch)
+        k, v = dev(b.k_new[layer], torch), dev(b.v_new[layer], torch)
+        if fused:
+            pkv.decode_attention_append_gqa(cache, Hq, layer, out, dev(q, torch), k, v, tables, lens_d, maxL, SCALE, ws)
+        else:
+            pkv.append(cache, layer, k, v, dev(b.positions, torch), dev(b.request_of_token, torch), tables)
+            pkv.decode_attention_gqa(cache, Hq, layer, out, dev(q, torch), tables, lens_d, maxL, SCALE, ws)
+        torch.cuda.synchronize()
+        return pool_d.cpu().numpy().view(np.uint16), out.cpu().numpy().view(np.uint16)
+
+    pool_a, out_a = run(False)
+    pool_b, out_b = run(True)
+    assert np.array_equal(pool_a, pool_b), "fused append differs from pkv_append"
+    assert np.array_equal(out_a, out_b), "fused grouped decode differs from append + decode"
