@@ -456,8 +456,8 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
 def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
     """Decode step over an 8-bit cache: the average mix's 32 rows over a
     32-layer, 7,152-block pool of FP8 E4M3 codes with one fp32 scale per
-    (token, head); per layer the 8-bit append of the 32 new tokens, then
-    decode.  Bytes = codes + scales of every cached token (8,448 B per token
+    (token, head); per layer the 8-bit append of the 32 new tokens fused into
+    decode (and, for comparison, the append as a launch of its own).  Bytes = codes + scales of every cached token (8,448 B per token
     and layer).  Codes are seeded random finite values: this leg times the
     kernels; parity and the quality cost are checked by the tests."""
     from workloads import SCALE
@@ -487,10 +487,14 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
     out = torch.empty((R, H, 128), dtype=torch.float16, device=dev)
     ws = torch.empty(pkv.decode_workspace_size_fp8(cache, R, maxL), dtype=torch.uint8, device=dev)
 
-    def step():
+    def step(fused=True):
         for l in range(NL):
-            pkv.append_fp8(cache, l, k[l], v[l], pos, rot, tables, stream=stream)
-            pkv.decode_attention_fp8(cache, l, out, q[l], tables, lens, maxL, SCALE, ws, stream=stream)
+            if fused:
+                pkv.decode_attention_append_fp8(cache, l, out, q[l], k[l], v[l], tables, lens, maxL, SCALE, ws,
+                                                stream=stream)
+            else:
+                pkv.append_fp8(cache, l, k[l], v[l], pos, rot, tables, stream=stream)
+                pkv.decode_attention_fp8(cache, l, out, q[l], tables, lens, maxL, SCALE, ws, stream=stream)
 
     for _ in range(warm):
         step()
@@ -502,6 +506,12 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    e0.record(stream)
+    for _ in range(steps):
+        step(fused=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_unfused = e0.elapsed_time(e1) / steps
     # the decode launch alone (decode + merge kernels), layers in turn
     launches = 4 * NL
     e0.record(stream)
@@ -518,6 +528,8 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
         "workload": f"average-mix decode step over an 8-bit cache: {R} rows x {NL} layers, {H} heads x 128, FP8 E4M3 "
                     f"codes + one fp32 scale per (token, head), {NB} blocks of 16 (append + decode per layer)",
         "ms_per_step": ms,
+        "step_path": "per layer one pkv_decode_attention_append_fp8 call",
+        "unfused_ms_per_step": ms_unfused,
         "kv_tokens_per_s": tokens / (ms / 1e3),
         "hbm_tb_s": nbytes / (ms / 1e3) / 1e12,
         "hbm_frac_of_peak": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,

@@ -408,6 +408,17 @@ int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, void* out, 
                              const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
                              int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
                              size_t workspace_bytes, void* stream);
+/* pkv_decode_attention_append for the 8-bit cache: row r's new token (FP16
+ * k_new[r], v_new[r], [num_rows][num_heads][128], 16-byte aligned) is
+ * quantized and written at position context_lens[r] - 1 exactly as
+ * pkv_append_fp8 would, and the result is pkv_decode_attention_fp8's: the
+ * same codes, scales and output bits as those two calls in sequence, in one
+ * launch fewer. */
+int pkv_decode_attention_append_fp8(const pkv_cache8* cache, int32_t layer, void* out, const void* q,
+                                    const void* k_new, const void* v_new, const int32_t* block_tables,
+                                    int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
+                                    int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

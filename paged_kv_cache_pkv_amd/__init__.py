@@ -340,6 +340,19 @@ def decode_workspace_size_fp8(cache: PagedCache8, num_rows: int, max_context_len
     return int(lib().pkv_decode_workspace_size_fp8(ctypes.byref(cache.desc), int(num_rows), int(max_context_len)))
 
 
+def decode_attention_append_fp8(cache: PagedCache8, layer: int, out, q, k_new, v_new, block_tables, context_lens,
+                                max_context_len: int, scale: float, workspace=None, stream=None):
+    """Quantize and append each row's new token at position context_lens[r] - 1, then decode (one fused launch)."""
+    R, stride = (int(x) for x in block_tables.shape)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_decode_attention_append_fp8(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2),
+                                                 _dptr(q, "q", 2), _dptr(k_new, "k_new", 2), _dptr(v_new, "v_new", 2),
+                                                 _dptr(block_tables, "block_tables", 4), stride,
+                                                 _dptr(context_lens, "context_lens", 4), R, int(max_context_len),
+                                                 float(scale), _dptr(workspace, "workspace"), ws_bytes,
+                                                 _stream_ptr(stream)))
+
+
 def decode_attention_fp8(cache: PagedCache8, layer: int, out, q, block_tables, context_lens, max_context_len: int,
                          scale: float, workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)

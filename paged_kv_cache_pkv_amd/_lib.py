@@ -73,6 +73,8 @@ SIGNATURES = {
     "pkv_decode_workspace_size_fp8": (c_size, [PkvCache8Desc_p, c_i32, c_i32]),
     "pkv_decode_attention_fp8": (ctypes.c_int, [PkvCache8Desc_p, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
                                                 ctypes.c_float, c_vp, c_size, c_vp]),
+    "pkv_decode_attention_append_fp8": (ctypes.c_int, [PkvCache8Desc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                                       c_vp, c_i32, c_i32, ctypes.c_float, c_vp, c_size, c_vp]),
     "pkv_block_bytes": (c_size, [PkvCacheDesc_p]),
     "pkv_copy_blocks": (ctypes.c_int, [PkvCacheDesc_p, c_vp, c_vp, c_i32, c_vp]),
     "pkv_swap_out": (ctypes.c_int, [PkvCacheDesc_p, c_i32_p, c_i32, c_vp, c_vp]),

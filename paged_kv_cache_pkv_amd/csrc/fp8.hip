@@ -94,6 +94,25 @@ __device__ __forceinline__ float max16(float v) {
   return v;
 }
 
+// Quantize one (token, head) row held by a 16-lane group (8 values per lane):
+// the row's amax over the group, the lane's 8 codes, and the row's scale.
+__device__ __forceinline__ u32x2 quantize_row8(const uint4& raw, float& scale) {
+  float x[8];
+  unpack8(raw, x);
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = max16(amax);
+  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lo |= (amax > 0.0f ? encode_e4m3(x[e] * inv) : 0u) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hi |= (amax > 0.0f ? encode_e4m3(x[4 + e] * inv) : 0u) << (8 * e);
+  scale = amax > 0.0f ? amax / 448.0f : 0.0f;
+  return u32x2{lo, hi};
+}
+
 // One workgroup per (new token, 16 of its 2 * num_heads K/V rows): 16 lanes
 // per row take 8 values each.  Every (token, row) is independent, so all of a
 // step's rows run at once rather than in passes behind each other's loads.
@@ -117,21 +136,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(
   const int b = block_tables[(size_t)r * bt_stride + (p >> 4)];
   if (b < 0 || b >= c.num_blocks) return;
   const int slot = p & 15;
-  float x[8];
-  unpack8(raw, x);
-  float amax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  amax = max16(amax);
-  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) lo |= (amax > 0.0f ? encode_e4m3(x[e] * inv) : 0u) << (8 * e);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) hi |= (amax > 0.0f ? encode_e4m3(x[4 + e] * inv) : 0u) << (8 * e);
+  float scale;
+  const u32x2 codes = quantize_row8(raw, scale);
   const size_t ri = row_index(b, layer, kv, h, slot, c.num_layers, c.num_heads);
-  *reinterpret_cast<uint2*>(c.codes + ri * kRowCodes + part * 8) = make_uint2(lo, hi);
-  if (part == 0) c.scales[ri] = amax > 0.0f ? amax / 448.0f : 0.0f;
+  *reinterpret_cast<u32x2*>(c.codes + ri * kRowCodes + part * 8) = codes;
+  if (part == 0) c.scales[ri] = scale;
 }
 
 struct F8Tile {
@@ -149,6 +158,8 @@ struct F8Args {
   const int32_t* context_lens;
   float* part_o;
   float2* part_ml;
+  const uint4* k_new;  // [R][H][16] FP16: each row's new token (appending decode only)
+  const uint4* v_new;
   int layer, bt_stride, num_rows, max_context_len, max_splits;
   float qk_scale;
 };
@@ -241,6 +252,10 @@ __device__ __forceinline__ void fold_f8(SoftmaxState& st, F8Tile& t, const uint4
   st.m = mn;
 }
 
+// kAppend: the range holding each row's last token quantizes that token from
+// k_new / v_new exactly as pkv_append_fp8 does, folds those codes and scales in
+// place of the slot's stale ones, and writes them into the slot.
+template <bool kAppend>
 __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
   const int head_groups = (a.c.num_heads + kF8Waves - 1) / kF8Waves;
   const int n = blockIdx.x;
@@ -276,6 +291,15 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
 
+  // the new token (slot ns of the last block: group ns / 4, entry ns % 4)
+  const bool takes_new = kAppend && split == nsplit - 1;
+  const int ns = (L - 1) & (kBlockSize - 1);
+  u32x2 nkc = u32x2{0u, 0u}, nvc = nkc;
+  float nks = 0.0f, nvs = 0.0f;
+  if (takes_new) {
+    nkc = quantize_row8(a.k_new[rh * 16 + chunk], nks);
+    nvc = quantize_row8(a.v_new[rh * 16 + chunk], nvs);
+  }
   constexpr int D = PKV_F8_DEPTH;  // blocks in registers: D - 1 loading while one folds
   F8Tile tile[D];
   bool ok[D];
@@ -294,6 +318,32 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
       if (jj + D - 1 < b1) issue(tile[(u + D - 1) % D], ok[(u + D - 1) % D], jj + D - 1);
       if (jj < b1) {
         const int valid = ok[u] ? min(L - jj * kBlockSize, kBlockSize) : 0;
+        if (takes_new && jj == nb - 1 && ok[u] && group == (ns >> 2)) {
+          const int e = ns & 3;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i == e) {
+              tile[u].k[i] = nkc;
+              tile[u].v[i] = nvc;
+            }
+          tile[u].sk.x = e == 0 ? nks : tile[u].sk.x;
+          tile[u].sk.y = e == 1 ? nks : tile[u].sk.y;
+          tile[u].sk.z = e == 2 ? nks : tile[u].sk.z;
+          tile[u].sk.w = e == 3 ? nks : tile[u].sk.w;
+          tile[u].sv.x = e == 0 ? nvs : tile[u].sv.x;
+          tile[u].sv.y = e == 1 ? nvs : tile[u].sv.y;
+          tile[u].sv.z = e == 2 ? nvs : tile[u].sv.z;
+          tile[u].sv.w = e == 3 ? nvs : tile[u].sv.w;
+          const int id = __builtin_amdgcn_readlane(my_id, jj - b0);
+          const size_t rk = row_index(id, a.layer, 0, h, ns, a.c.num_layers, a.c.num_heads);
+          const size_t rv = row_index(id, a.layer, 1, h, ns, a.c.num_layers, a.c.num_heads);
+          *reinterpret_cast<u32x2*>(a.c.codes + rk * kRowCodes + chunk * 8) = nkc;
+          *reinterpret_cast<u32x2*>(a.c.codes + rv * kRowCodes + chunk * 8) = nvc;
+          if (chunk == 0) {
+            a.c.scales[rk] = nks;
+            a.c.scales[rv] = nvs;
+          }
+        }
         if (valid == kBlockSize)
           fold_f8<false>(st, tile[u], q, a.qk_scale, group, valid);
         else
@@ -393,11 +443,13 @@ extern "C" size_t pkv_decode_workspace_size_fp8(const pkv_cache8* cache, int32_t
   return align256(n * kHeadDim * sizeof(float)) + align256(n * sizeof(float2));
 }
 
-extern "C" int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, void* out, const void* q,
-                                        const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
-                                        int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
-  using namespace pkv;
+namespace pkv {
+namespace {
+
+int decode_fp8_launch(const pkv_cache8* cache, int32_t layer, void* out, const void* q, const void* k_new,
+                      const void* v_new, const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                      int32_t num_rows, int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (int rc = check_cache8(cache)) return rc;
   if (layer < 0 || layer >= cache->num_layers) return fail(PKV_ERR_INVALID_ARG, "layer out of range");
   if (num_rows < 1) return fail(PKV_ERR_INVALID_ARG, "num_rows must be >= 1");
@@ -425,6 +477,8 @@ extern "C" int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, 
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = workspace ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + align256(n * kHeadDim * sizeof(float)))
                         : nullptr;
+  a.k_new = static_cast<const uint4*>(k_new);
+  a.v_new = static_cast<const uint4*>(v_new);
   a.layer = layer;
   a.bt_stride = bt_stride;
   a.num_rows = num_rows;
@@ -436,11 +490,38 @@ extern "C" int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, 
   int64_t rs_total = ((int64_t)num_rows * ms + kF8Xcds - 1) / kF8Xcds * kF8Xcds;
   const int64_t wgs = rs_total * head_groups;
   if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-  decode_fp8_kernel<<<dim3((unsigned)wgs), dim3(kF8Threads), 0, s>>>(a);
+  if (k_new)
+    decode_fp8_kernel<true><<<dim3((unsigned)wgs), dim3(kF8Threads), 0, s>>>(a);
+  else
+    decode_fp8_kernel<false><<<dim3((unsigned)wgs), dim3(kF8Threads), 0, s>>>(a);
   if (int rc = check_launch("decode fp8 kernel")) return rc;
   if (ms > 1) {
     merge_fp8_kernel<<<dim3(num_rows, head_groups), dim3(kF8Threads), 0, s>>>(a);
     if (int rc = check_launch("merge fp8 kernel")) return rc;
   }
   return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, void* out, const void* q,
+                                        const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                                        int32_t num_rows, int32_t max_context_len, float scale, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return pkv::decode_fp8_launch(cache, layer, out, q, nullptr, nullptr, block_tables, bt_stride, context_lens,
+                                num_rows, max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_decode_attention_append_fp8(const pkv_cache8* cache, int32_t layer, void* out, const void* q,
+                                               const void* k_new, const void* v_new, const int32_t* block_tables,
+                                               int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
+                                               int32_t max_context_len, float scale, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+  using namespace pkv;
+  if (!k_new || !v_new) return fail(PKV_ERR_INVALID_ARG, "null device pointer");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  return decode_fp8_launch(cache, layer, out, q, k_new, v_new, block_tables, bt_stride, context_lens, num_rows,
+                           max_context_len, scale, workspace, workspace_bytes, stream);
 }

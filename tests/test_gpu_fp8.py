@@ -147,3 +147,37 @@ def test_fp8_quality_against_fp16():
         s = compare(got[r], ref16[r])
         say(f"fp8 vs fp16 attention, context {L}: max_abs {s['max_abs']:.2e}, rms {np.sqrt(np.mean((got[r] - ref16[r]) ** 2)):.2e}")
         assert s["max_abs"] < 0.05
+
+
+def test_fp8_appending_decode_equals_append_then_decode_bitwise():
+    """pkv_decode_attention_append_fp8 leaves the same codes and scales and the
+    same output bits as pkv_append_fp8 followed by pkv_decode_attention_fp8."""
+    torch = torch_cuda()
+    lens = [1, 4, 5, 16, 17, 255, 256, 257, 700, 2600]
+    b = build_batch("fp8-fused", 39, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 6,
+                    num_layers=2, num_heads=32, stride=max(-(-L // 16) for L in lens) + 2)
+    codes, scales = _quantized_pool(b.pool)
+    layer = 1
+    R, maxL = len(lens), max(lens)
+    say(f"fp8 appending decode vs append + decode, lens={lens}")
+
+    def run(fused):
+        cache, codes_d, scales_d = _gpu_cache(torch, codes, scales)
+        ws = torch.empty(pkv.decode_workspace_size_fp8(cache, R, maxL), dtype=torch.uint8, device="cuda")
+        out = torch.empty((R, 32, 128), dtype=torch.float16, device="cuda")
+        tabs, lens_d = dev(b.block_tables, torch), dev(b.context_lens, torch)
+        k, v = dev(b.k_new[layer], torch), dev(b.v_new[layer], torch)
+        if fused:
+            pkv.decode_attention_append_fp8(cache, layer, out, dev(b.q[layer], torch), k, v, tabs, lens_d, maxL,
+                                            SCALE, ws)
+        else:
+            pkv.append_fp8(cache, layer, k, v, dev(b.positions, torch), dev(b.request_of_token, torch), tabs)
+            pkv.decode_attention_fp8(cache, layer, out, dev(b.q[layer], torch), tabs, lens_d, maxL, SCALE, ws)
+        torch.cuda.synchronize()
+        return (codes_d.cpu().numpy(), scales_d.cpu().numpy().view(np.uint32), out.cpu().numpy().view(np.uint16))
+
+    ca, sa, oa = run(False)
+    cb, sb, ob = run(True)
+    assert np.array_equal(ca, cb), "fused 8-bit append codes differ"
+    assert np.array_equal(sa, sb), "fused 8-bit append scales differ"
+    assert np.array_equal(oa, ob), "fused 8-bit decode differs from append + decode"
