@@ -23,7 +23,7 @@ import dataclasses
 
 import numpy as np
 
-from . import (BLOCK_SIZE, BlockPool, PagedCache, append, decode_attention, decode_attention_prefix,
+from . import (BLOCK_SIZE, BlockPool, PagedCache, append, decode_attention_append, decode_attention_prefix,
                decode_workspace_size, decode_workspace_size_prefix)
 
 
@@ -167,13 +167,14 @@ class ContinuousBatchTrace:
         rot_d = torch.arange(R, dtype=torch.int32, device=self.dev)
         lens_d = torch.from_numpy(lens).to(self.dev)
         out = torch.empty((R, self.H, 128), dtype=torch.float16, device=self.dev)
-        append(self.cache, 0, k, v, pos_d, rot_d, tab_d)
         if self.shared_decode:
+            append(self.cache, 0, k, v, pos_d, rot_d, tab_d)
             marks = torch.from_numpy(np.array([1 if r.shared else 0 for r in self.rows], dtype=np.int32)).to(self.dev)
             decode_attention_prefix(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, marks,
                                     self.prefix_tokens // BLOCK_SIZE, self.ws)
         else:
-            decode_attention(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, self.ws)
+            # each row's new token is appended by the decode launch itself
+            decode_attention_append(self.cache, 0, out, q, k, v, tab_d, lens_d, self.max_ctx, self.scale, self.ws)
         if events:
             events[2].record()
         snap = {"step": self.step_no, "reqs": [r.req for r in self.rows], "lens": lens.copy(),
