@@ -249,3 +249,35 @@ def test_validation_block_copies():
     assert L.pkv_swap_out(ctypes.byref(d), p, -2, FAKE, None) == -1
     assert L.pkv_swap_out(ctypes.byref(d), p, 1, None, None) == -1
     assert L.pkv_swap_in(ctypes.byref(d), None, p, 1, None) == -1
+
+
+def test_validation_appending_decodes():
+    """The fused append + decode calls check their extra arguments before any
+    launch, and otherwise validate exactly as the plain decode calls do."""
+    L = pkv.lib()
+    d = _desc(num_heads=8)
+
+    def call(k=FAKE, v=FAKE, layer=0, R=4, maxL=256, Hq=None):
+        if Hq is None:
+            return L.pkv_decode_attention_append(ctypes.byref(d), layer, FAKE, FAKE, k, v, FAKE, 16, FAKE, R, maxL,
+                                                 0.088, FAKE, 1 << 20, None)
+        return L.pkv_decode_attention_append_gqa(ctypes.byref(d), Hq, layer, FAKE, FAKE, k, v, FAKE, 16, FAKE, R,
+                                                 maxL, 0.088, FAKE, 1 << 20, None)
+    assert call(k=None) == -1
+    assert call(v=None) == -1
+    assert call(k=ctypes.c_void_p(0x200008)) == -1  # misaligned new keys
+    assert call(layer=1) == -1
+    assert call(R=0) == -1
+    assert call(maxL=16 * 16 + 1) == -1
+    assert call(Hq=24) == -2    # 3 query heads per KV head is not a supported group
+    assert call(Hq=8 * 16) == -2
+    assert call(Hq=32, k=None) == -1
+    assert L.pkv_decode_attention_append(None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 256, 0.088, FAKE, 1 << 20,
+                                         None) == -1
+    d8 = _lib.PkvCache8Desc(ctypes.c_void_p(0x100000), ctypes.c_void_p(0x300000), 64, 1, 32, 16, 128)
+    assert L.pkv_decode_attention_append_fp8(ctypes.byref(d8), 0, FAKE, FAKE, None, FAKE, FAKE, 16, FAKE, 4, 256,
+                                             0.088, FAKE, 1 << 20, None) == -1
+    assert L.pkv_decode_attention_append_fp8(ctypes.byref(d8), 0, FAKE, FAKE, ctypes.c_void_p(0x200004), FAKE, FAKE,
+                                             16, FAKE, 4, 256, 0.088, FAKE, 1 << 20, None) == -1
+    assert L.pkv_decode_attention_append_fp8(ctypes.byref(d8), 1, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 256,
+                                             0.088, FAKE, 1 << 20, None) == -1
