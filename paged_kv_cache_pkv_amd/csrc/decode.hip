@@ -23,7 +23,7 @@
 // (v_dot2_f32_f16), summed over the 16 lanes of a token with DPP moves.  Each
 // group of 16 lanes keeps its own online-softmax state over its four tokens
 // of every block; the four groups merge once at the end of the range.  Blocks
-// are software-pipelined two ahead so a wave keeps 24 KiB in flight.
+// are software-pipelined three ahead so a wave keeps 32 KiB in flight.
 
 #include "decode_core.h"
 
@@ -31,7 +31,7 @@ namespace pkv {
 namespace {
 
 #ifndef PKV_WAVES
-#define PKV_WAVES 8
+#define PKV_WAVES 4
 #endif
 #ifndef PKV_XCD_REMAP
 #define PKV_XCD_REMAP 1
@@ -64,10 +64,10 @@ struct DecodeArgs {
 // the range holding it also writes it into its pool slot (the step's append).
 template <bool kAppend>
 __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_kernel(DecodeArgs a) {
-  // 1-D grid over (row, range, head group).  Workgroups go to the XCDs
-  // round-robin by index; with the remap, the head groups of one (row,
-  // range) land on one XCD back to back, so they share its L2 and TLB for
-  // the same block slabs.
+  // 1-D grid over (row, range, group of kWavesPerGroup heads).  Workgroups go
+  // to the XCDs round-robin by index; with the remap, the head groups of one
+  // (row, range) land on one XCD back to back, so they share its L2 and TLB
+  // for the same block slabs.
   const int head_groups = (a.num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
   const int n = blockIdx.x;
 #if PKV_XCD_REMAP

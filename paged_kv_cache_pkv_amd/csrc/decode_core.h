@@ -13,7 +13,7 @@ namespace pkv {
 #define PKV_SPLIT_BLOCKS 16
 #endif
 #ifndef PKV_PREFETCH
-#define PKV_PREFETCH 2
+#define PKV_PREFETCH 3
 #endif
 // Cache-policy bits of the K/V buffer loads: 2 = nt (streaming).  Keys and
 // values are read once per step, and on gfx950 the non-temporal policy lifts
