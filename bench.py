@@ -307,10 +307,12 @@ def measure_block_copies(torch, pkv, cache, free_ids, stream, n=64, reps=10):
     }
 
 
-def measure_tiny(torch, pkv, dev, stream, reps=50):
+def measure_tiny(torch, pkv, dev, stream, reps=50, cold_reps=10):
     """The tiny decode configuration (4 rows with contexts 17/40/100/256, one
-    layer, 64-block pool): append + decode per step.  Its 6.8 MB stay in the
-    caches, so this is the path's launch latency, not a bandwidth figure."""
+    layer, 64-block pool): append + decode per step, also as the one fused
+    call.  Its 6.8 MB stay in the caches, so this is the path's launch
+    latency, not a bandwidth figure; the cold-cache figure scrubs the 256 MB
+    last-level cache (a 512 MB streaming write) before each timed step."""
     from workloads import SCALE, c1_tiny
 
     b = c1_tiny(seed=0)
@@ -331,17 +333,38 @@ def measure_tiny(torch, pkv, dev, stream, reps=50):
         pkv.append(cache, 0, k, v, pos, rot, tables, stream=stream)
         pkv.decode_attention(cache, 0, out, q, tables, lens, maxL, SCALE, ws, stream=stream)
 
-    step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    def fused():
+        pkv.decode_attention_append(cache, 0, out, q, k, v, tables, lens, maxL, SCALE, ws, stream=stream)
+
+    def warm(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    def cold(fn):
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        us = []
+        for _ in range(cold_reps):
+            scrub.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+        del scrub
+        return float(np.median(us))
+
     return {"workload": "4 rows, contexts 17/40/100/256, one layer, 64-block pool: append + decode",
-            "us_per_step": ms * 1e3, "kv_tokens": int(b.context_lens.sum())}
+            "us_per_step": warm(step), "us_per_step_fused": warm(fused),
+            "cold_cache_us_per_step": cold(step), "cold_cache_us_per_step_fused": cold(fused),
+            "kv_tokens": int(b.context_lens.sum())}
 
 
 def measure_long_context(torch, pkv, cache, stream, steps=5, warm=2):
