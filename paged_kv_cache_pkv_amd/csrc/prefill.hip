@@ -354,6 +354,14 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
         const h8 va = bitcast<h8>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kk], o[dt], 0, 0, 0);
       }
+    // Transposed V reads run two MFMAs ahead: four up front, then two (the
+    // next MFMA's operand) after each MFMA while any remain.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA
+      if (j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // two LDS reads
+    }
   };
   // One half step: the QK^T of the next half step (into s_next) on the
   // matrix cores while this half step's softmax (of s_cur) runs on the
@@ -371,11 +379,12 @@ __device__ void prefill_tile(const PrefillArgs& a, int r_in, int qtile_in, int h
     const float mstep = step_max(s_cur);
     h8 pb[2];
     float ls = weights(s_cur, pb);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    // All eight K operand reads go out before the first MFMA that needs one:
+    // the LDS latency then overlaps the chain instead of stalling each link.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // eight LDS reads
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if (j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
       __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // two transcendental
     }
