@@ -307,6 +307,17 @@ def measure_block_copies(torch, pkv, cache, free_ids, stream, n=64, reps=10):
     }
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def measure_tiny(torch, pkv, dev, stream, reps=50, cold_reps=10):
     """The tiny decode configuration (4 rows with contexts 17/40/100/256, one
     layer, 64-block pool): append + decode per step, also as the one fused
@@ -630,8 +641,11 @@ def main():
     cpu_sample = None
     if not args.no_cpu_baseline:
         ids = np.unique(np.concatenate([tables[r, :tlen[r]] for r in range(R)]))
+        torch.cuda.synchronize()
+        t_d2h = time.perf_counter()
         slab = pool_d[torch.from_numpy(ids.astype(np.int64)).to(dev), 0].cpu().numpy().view(np.uint16)
-        cpu_sample = (ids, slab)
+        t_d2h = time.perf_counter() - t_d2h
+        cpu_sample = (ids, slab, t_d2h)
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -743,7 +757,7 @@ def main():
 
         import oracle.paged as opaged
 
-        ids, slab = cpu_sample
+        ids, slab, t_d2h = cpu_sample
         index = {int(bk): i for i, bk in enumerate(ids)}
 
         class Blocks:
@@ -757,6 +771,7 @@ def main():
             slab[index[bk], 0, :, s, :] = batch.k_new[0, r]
             slab[index[bk], 1, :, s, :] = batch.v_new[0, r]
         t0 = time.perf_counter()
+        c0 = time.process_time()
         rows_done = tok_done = bad = 0
         max_abs = 0.0
         while time.perf_counter() - t0 < args.cpu_seconds and rows_done < 64 * R:
@@ -769,12 +784,19 @@ def main():
                 max_abs = max(max_abs, float(err.max()))
                 bad += int((err > np.maximum(2e-3, 1e-2 * np.abs(ref))).sum())
         cpu_s = time.perf_counter() - t0
+        busy_s = time.process_time() - c0
         parity = {"layer": 0, "rows": min(rows_done, R), "max_abs": max_abs, "bad": bad, "pass": bad == 0}
         threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-        cpu_baseline = {"value": (tok_done / NL) / cpu_s, "unit": "KV-tokens/s", "cores": int(threads),
+        cpu_baseline = {"value": (tok_done / NL) / cpu_s, "unit": "KV-tokens/s",
+                        "cores": max(1, int(round(busy_s / cpu_s))),
                         "kind": "oracle",
                         "sample": f"fp64 oracle decode of {rows_done} (row, layer-0) tasks of the same step, "
-                                  f"{tok_done} one-layer tokens in {cpu_s:.1f} s; value = layer-tokens / 32 / s"}
+                                  f"{tok_done} one-layer tokens in {cpu_s:.1f} s; value = layer-tokens / 32 / s",
+                        "cores_note": "process CPU time / wall time over the timed oracle run",
+                        "cpu_seconds": busy_s, "wall_seconds": cpu_s, "blas_threads": int(threads),
+                        "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+                        "d2h_readback_s": t_d2h,
+                        "d2h_note": "the sample's blocks (layer 0) copied to host memory before the run, not timed in it"}
 
     blocks = None
     long_ctx = None
