@@ -58,6 +58,8 @@ CASES = [
     ("one-head-long", 1, 1, [4100, 8192]),
     # more than 64 ranges per row: the merge takes its ranges in several passes of 64
     ("beyond-64-ranges", 2, 1, [20000, 16400, 16385, 7]),
+    # the most heads the library accepts (32 workgroups of 4 heads per range)
+    ("max-heads", 128, 2, [300, 17, 1]),
 ]
 
 

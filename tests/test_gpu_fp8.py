@@ -56,16 +56,20 @@ def test_append_fp8_bitexact(which):
 
 
 CASES = [
-    ("ragged", 1, [1, 2, 15, 16, 17, 100, 255, 256, 257, 512]),
-    ("multi-split", 2, [513, 1025, 2600]),
+    # name, heads, layers, lens
+    ("ragged", 32, 1, [1, 2, 15, 16, 17, 100, 255, 256, 257, 512]),
+    ("multi-split", 32, 2, [513, 1025, 2600]),
+    ("odd-heads", 5, 1, [300, 1, 700]),
+    # the most heads the library accepts
+    ("max-heads", 128, 1, [300, 17]),
 ]
 
 
-@pytest.mark.parametrize("name,layers,lens", CASES, ids=[c[0] for c in CASES])
-def test_decode_fp8_parity(name, layers, lens):
+@pytest.mark.parametrize("name,heads,layers,lens", CASES, ids=[c[0] for c in CASES])
+def test_decode_fp8_parity(name, heads, layers, lens):
     torch = torch_cuda()
     b = build_batch(f"fp8-{name}", 31, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 4,
-                    num_layers=layers, num_heads=32, stride=max(-(-L // 16) for L in lens))
+                    num_layers=layers, num_heads=heads, stride=max(-(-L // 16) for L in lens))
     pool = b.pool
     for layer in range(layers):
         pool = opaged.append(pool, layer, b.k_new[layer], b.v_new[layer], b.positions, b.request_of_token,
@@ -75,9 +79,9 @@ def test_decode_fp8_parity(name, layers, lens):
     R = len(lens)
     maxL = max(lens)
     ws = torch.empty(max(pkv.decode_workspace_size_fp8(cache, R, maxL), 256), dtype=torch.uint8, device="cuda")
-    out = torch.empty((R, 32, 128), dtype=torch.float16, device="cuda")
+    out = torch.empty((R, heads, 128), dtype=torch.float16, device="cuda")
     for layer in range(layers):
-        say(f"decode fp8 {name} layer {layer}")
+        say(f"decode fp8 {name} heads={heads} layer {layer}")
         pkv.decode_attention_fp8(cache, layer, out, dev(b.q[layer], torch), dev(b.block_tables, torch),
                                  dev(b.context_lens, torch), maxL, SCALE, ws)
         torch.cuda.synchronize()

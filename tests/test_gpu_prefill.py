@@ -46,6 +46,8 @@ CASES = [
     ("odd-heads", 5, [900, 33, 2049], [257, 1, 3]),
     # a decode row of 67 ranges and a chunk of 9 prefill ranges, merged in the same call
     ("long-rows", 2, [17000, 18200, 600], [1, 140, 300]),
+    # the most KV heads the pool accepts
+    ("max-heads", 128, [300, 40], [70, 1]),
 ]
 
 
