@@ -186,32 +186,37 @@ def _run_trace(torch, steps, warm, shared_decode):
     torch.cuda.synchronize()
     rec = []
     for _ in range(steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         snap = tr.step(events=ev)
         sharers = sum(1 for r in tr.rows if r.shared)
-        rec.append((ev, int(snap["lens"].sum()), sharers))
+        rec.append((ev, int(snap["lens"].sum()), sharers, snap["host_ms"]))
     torch.cuda.synchronize()
-    fill_ms = np.array([e[0].elapsed_time(e[1]) for e, _, _ in rec])
-    step_ms = np.array([e[1].elapsed_time(e[2]) for e, _, _ in rec])
-    tokens = np.array([t for _, t, _ in rec], dtype=np.float64)
-    sharers = np.array([n for _, _, n in rec], dtype=np.float64)
+    fill_ms = np.array([e[0].elapsed_time(e[1]) for e, _, _, _ in rec])
+    step_ms = np.array([e[2].elapsed_time(e[3]) for e, _, _, _ in rec])
+    with_host_ms = np.array([e[1].elapsed_time(e[3]) for e, _, _, _ in rec])
+    host_ms = np.array([h for _, _, _, h in rec])
+    tokens = np.array([t for _, t, _, _ in rec], dtype=np.float64)
+    sharers = np.array([n for _, _, n, _ in rec], dtype=np.float64)
     joins = sum(1 for j in tr.log["joins"] if j[4] >= warm)
     prefix = tr.prefix_tokens
     tr.drain()
     assert tr.pool.num_free == 36864, "trace leaked blocks"
-    return step_ms, fill_ms, tokens, sharers, joins, prefix
+    return step_ms, fill_ms, tokens, sharers, joins, prefix, with_host_ms, host_ms
 
 
 def measure_trace(torch, steps=300, warm=5):
     """Continuous-batching trace: up to 64 rows over a 36,864-block one-layer
     pool, prompts U{50..8000}, answers U{1..1000}, a 2,000-token prefix
     shared by reference counts; rows leave and are refilled every step.
-    The decode part of a step (grow, append one token per row, decode) is
-    timed with events separately from the fill of joining rows.  The same
-    seeded trace runs twice: with plain decode, and with the shared-prefix
-    decode that reads the prefix once per step for every 32 rows holding it."""
-    step_ms, fill_ms, tokens, sharers, joins, prefix = _run_trace(torch, steps, warm, False)
-    s_ms, _, s_tokens, s_sharers, _, _ = _run_trace(torch, steps, warm, True)
+    The decode part of a step (append one token per row, decode) is timed
+    with events around its launches, separately from the fill of joining
+    rows; the host work before the launches (table growth, the step's
+    synthetic inputs and their pageable upload) is timed on the host and
+    reported beside it, as is the step with it.  The same seeded trace runs
+    twice: with plain decode, and with the shared-prefix decode that reads
+    the prefix once per step for every 32 rows holding it."""
+    step_ms, fill_ms, tokens, sharers, joins, prefix, wh_ms, host_ms = _run_trace(torch, steps, warm, False)
+    s_ms, _, s_tokens, s_sharers, _, _, s_wh_ms, s_host_ms = _run_trace(torch, steps, warm, True)
     assert np.array_equal(tokens, s_tokens) and np.array_equal(sharers, s_sharers), "the two traces diverged"
     # tokens the shared-prefix decode reads: the prefix once per tile of up to 32 sharing rows
     physical = tokens - prefix * (sharers - np.ceil(sharers / 32.0))
@@ -222,6 +227,8 @@ def measure_trace(torch, steps=300, warm=5):
         "decode_step_ms_p50": float(np.percentile(step_ms, 50)),
         "decode_step_ms_p90": float(np.percentile(step_ms, 90)),
         "decode_step_ms_max": float(step_ms.max()),
+        "decode_step_with_host_ms_p50": float(np.percentile(wh_ms, 50)),
+        "host_prep_ms_p50": float(np.percentile(host_ms, 50)),
         "logical_kv_tokens_per_step_mean": float(tokens.mean()),
         "kv_tokens_per_s": float(tokens.sum() / (step_ms.sum() / 1e3)),
         "logical_tb_s": float(tokens.sum() * LAYER_TOKEN_BYTES / (step_ms.sum() / 1e3) / 1e12),
@@ -232,6 +239,8 @@ def measure_trace(torch, steps=300, warm=5):
             "decode_step_ms_p50": float(np.percentile(s_ms, 50)),
             "decode_step_ms_p90": float(np.percentile(s_ms, 90)),
             "decode_step_ms_max": float(s_ms.max()),
+            "decode_step_with_host_ms_p50": float(np.percentile(s_wh_ms, 50)),
+            "host_prep_ms_p50": float(np.percentile(s_host_ms, 50)),
             "sharing_rows_per_step_mean": float(sharers.mean()),
             "read_kv_tokens_per_step_mean": float(physical.mean()),
             "kv_tokens_per_s": float(tokens.sum() / (s_ms.sum() / 1e3)),

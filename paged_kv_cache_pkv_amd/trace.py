@@ -21,6 +21,8 @@ from __future__ import annotations
 
 import dataclasses
 
+import time
+
 import numpy as np
 
 from . import (BLOCK_SIZE, BlockPool, PagedCache, append, decode_attention_append, decode_attention_prefix,
@@ -143,8 +145,11 @@ class ContinuousBatchTrace:
 
     def step(self, events=None):
         """Leave, join, grow, append one token per row, decode.  Returns the
-        step's row snapshot (for checkers) and, with events=(start, mid, end),
-        records them around the fill and the decode part."""
+        step's row snapshot (for checkers).  With events=(start, filled,
+        launch, end) it records them around the fill of joining rows and
+        around the decode part's launches; the host work in between (table
+        growth, the step's synthetic inputs and their upload) is timed on the
+        host and returned as snap["host_ms"]."""
         torch = self.torch
         finished = [r for r in self.rows if r.generated >= r.answer]
         for r in finished:
@@ -156,6 +161,7 @@ class ContinuousBatchTrace:
             self.rows.append(self._join(*self._draw_request()))
         if events:
             events[1].record()
+        t_host = time.perf_counter()
         R = len(self.rows)
         for r in self.rows:  # the new token sits at position r.length
             r.nblk = self.pool.grow(r.table, r.nblk, r.length + 1)
@@ -168,17 +174,22 @@ class ContinuousBatchTrace:
         lens_d = torch.from_numpy(lens).to(self.dev)
         out = torch.empty((R, self.H, 128), dtype=torch.float16, device=self.dev)
         if self.shared_decode:
-            append(self.cache, 0, k, v, pos_d, rot_d, tab_d)
             marks = torch.from_numpy(np.array([1 if r.shared else 0 for r in self.rows], dtype=np.int32)).to(self.dev)
+        host_ms = (time.perf_counter() - t_host) * 1e3
+        if events:
+            events[2].record()
+        if self.shared_decode:
+            append(self.cache, 0, k, v, pos_d, rot_d, tab_d)
             decode_attention_prefix(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, marks,
                                     self.prefix_tokens // BLOCK_SIZE, self.ws)
         else:
             # each row's new token is appended by the decode launch itself
             decode_attention_append(self.cache, 0, out, q, k, v, tab_d, lens_d, self.max_ctx, self.scale, self.ws)
         if events:
-            events[2].record()
+            events[3].record()
         snap = {"step": self.step_no, "reqs": [r.req for r in self.rows], "lens": lens.copy(),
-                "gen_index": [r.generated for r in self.rows], "tables": tables.copy(), "out": out}
+                "gen_index": [r.generated for r in self.rows], "tables": tables.copy(), "out": out,
+                "host_ms": host_ms}
         self.log["steps"].append({"step": self.step_no, "reqs": snap["reqs"], "lens": lens.copy(),
                                   "new_pos": (lens - 1).copy()})
         for r in self.rows:
