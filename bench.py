@@ -36,31 +36,42 @@ LAYER_TOKEN_BYTES = 2 * 32 * 128 * 2          # K+V of one token, one layer
 STEP_TOKEN_BYTES = LAYER_TOKEN_BYTES * 32       # all 32 layers
 
 
+CSRC = os.path.join(ROOT, "paged_kv_cache_pkv_amd", "csrc")
 COUNTERS = os.path.join(ROOT, "profiles", "decode_average_mix_hbm_counters.json")
-DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_pkv_amd", "csrc", n) for n in ("decode.hip", "decode_core.h", "device_common.h")]
+DECODE_SOURCES = [os.path.join(CSRC, n) for n in ("decode.hip", "decode_core.h", "device_common.h")]
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_chunk512_hbm_counters.json")
+PREFILL_SOURCES = [os.path.join(CSRC, n) for n in ("prefill.hip", "decode_core.h", "device_common.h")]
+APPEND_COUNTERS = os.path.join(ROOT, "profiles", "append_bulk_hbm_counters.json")
+APPEND_SOURCES = [os.path.join(CSRC, n) for n in ("append.hip", "device_common.h")]
 
 
-def source_digest() -> str:
+def source_digest(sources=None) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for p in DECODE_SOURCES:
+    for p in sources or DECODE_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def counted_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None when the decode kernel source has changed since it was taken."""
+def counted_record(path, sources):
+    """A committed rocprofv3 counter summary (JSON), or None when it is missing
+    or the kernel sources have changed since the counters were taken."""
     try:
-        with open(COUNTERS) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_digest():
+    if rec.get("source_sha256") != source_digest(sources):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def counted_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None."""
+    rec = counted_record(COUNTERS, DECODE_SOURCES)
+    return rec.get("traffic_bytes_per_launch") if rec else None
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0
@@ -147,8 +158,10 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         gbs = tokens * 2 * LAYER_TOKEN_BYTES / (ms / 1e3) / 1e9  # each K/V byte read once, written once
+        rec = counted_record(APPEND_COUNTERS, APPEND_SOURCES)
+        traffic = rec.get("traffic_bytes_per_launch_by_tokens", {}).get(str(tokens)) if rec else None
         return {"tokens": tokens, "us": ms * 1e3, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS}
+                "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}
 
     mixed = c5_mixed(with_pool=False)
     chunk = build_batch("chunk-only", 4, [8000], [512], num_blocks=7152, with_pool=False, stride=520)
@@ -159,6 +172,8 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
     flops = prefill_flops(chunk)
     kv_mixed = float(mixed.context_lens.sum()) * LAYER_TOKEN_BYTES
     tflops = flops / (chunk_ms / 1e3) / 1e12
+    rec = counted_record(PREFILL_COUNTERS, PREFILL_SOURCES)
+    prefill_traffic = rec.get("traffic_bytes_per_launch") if rec else None
     return {
         "workload": "512-token causal chunk at offset 7488 of an 8000-token prompt + 31 average-mix decode rows, "
                     "one layer, 32 heads x 128, FP16",
@@ -171,7 +186,7 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
         "append_543_tokens_us": app_mixed_ms * 1e3,
         "append_bulk_roofline": appends,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                     "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": prefill_traffic,
                      "kernel": "pkv_chunked_prefill_attention on the chunk alone (tile + merge launches)"},
     }
 
