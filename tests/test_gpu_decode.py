@@ -169,15 +169,16 @@ def test_decode_growing_scores():
     say(f"  {s}")
 
 
-def test_appending_decode_equals_append_then_decode_bitwise():
+@pytest.mark.parametrize("heads", [32, 5])
+def test_appending_decode_equals_append_then_decode_bitwise(heads):
     """pkv_decode_attention_append leaves the same pool bytes and the same
     output bits as pkv_append followed by pkv_decode_attention, for rows that
     end on, just past and inside block and range boundaries, in the second
-    layer of a two-layer pool."""
+    layer of a two-layer pool (5 heads: a workgroup with idle waves)."""
     torch = torch_cuda()
     lens = [1, 16, 17, 255, 256, 257, 700, 2600]
     b = build_batch("fused", 61, lens, np.ones(len(lens)), num_blocks=sum(-(-L // 16) for L in lens) + 6,
-                    num_layers=2, stride=max(-(-L // 16) for L in lens) + 2)
+                    num_layers=2, num_heads=heads, stride=max(-(-L // 16) for L in lens) + 2)
     layer = 1
     say(f"appending decode vs append + decode, lens={lens}")
     _, ref_bits = gpu_decode(b, torch, layer=layer)
@@ -187,7 +188,7 @@ def test_appending_decode_equals_append_then_decode_bitwise():
     cache = pkv.PagedCache(pool_d)
     R, maxL = len(lens), max(lens)
     ws = torch.empty(pkv.decode_workspace_size(cache, R, maxL), dtype=torch.uint8, device="cuda")
-    out = torch.empty((R, 32, 128), dtype=torch.float16, device="cuda")
+    out = torch.empty((R, heads, 128), dtype=torch.float16, device="cuda")
     pkv.decode_attention_append(cache, layer, out, dev(b.q[layer], torch), dev(b.k_new[layer], torch),
                                 dev(b.v_new[layer], torch), dev(b.block_tables, torch), dev(b.context_lens, torch),
                                 maxL, SCALE, ws)

@@ -153,13 +153,15 @@ def test_fp8_quality_against_fp16():
         assert s["max_abs"] < 0.05
 
 
-def test_fp8_appending_decode_equals_append_then_decode_bitwise():
+@pytest.mark.parametrize("heads", [32, 5])
+def test_fp8_appending_decode_equals_append_then_decode_bitwise(heads):
     """pkv_decode_attention_append_fp8 leaves the same codes and scales and the
-    same output bits as pkv_append_fp8 followed by pkv_decode_attention_fp8."""
+    same output bits as pkv_append_fp8 followed by pkv_decode_attention_fp8
+    (5 heads: a workgroup whose last waves hold no head)."""
     torch = torch_cuda()
     lens = [1, 4, 5, 16, 17, 255, 256, 257, 700, 2600]
     b = build_batch("fp8-fused", 39, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 6,
-                    num_layers=2, num_heads=32, stride=max(-(-L // 16) for L in lens) + 2)
+                    num_layers=2, num_heads=heads, stride=max(-(-L // 16) for L in lens) + 2)
     codes, scales = _quantized_pool(b.pool)
     layer = 1
     R, maxL = len(lens), max(lens)
@@ -168,7 +170,7 @@ def test_fp8_appending_decode_equals_append_then_decode_bitwise():
     def run(fused):
         cache, codes_d, scales_d = _gpu_cache(torch, codes, scales)
         ws = torch.empty(pkv.decode_workspace_size_fp8(cache, R, maxL), dtype=torch.uint8, device="cuda")
-        out = torch.empty((R, 32, 128), dtype=torch.float16, device="cuda")
+        out = torch.empty((R, heads, 128), dtype=torch.float16, device="cuda")
         tabs, lens_d = dev(b.block_tables, torch), dev(b.context_lens, torch)
         k, v = dev(b.k_new[layer], torch), dev(b.v_new[layer], torch)
         if fused:
