@@ -73,6 +73,11 @@ def _case(name):
         lens = [40, 17, 300, 33, 16, 5, 2000]
         shared = [1, 2, 3, 6]
         lone = [4]                 # L = 16 = 16 P
+    elif name == "heads-12":        # a suffix workgroup of 8 heads with only 4 in use
+        P, layers, H = 20, 1, 12
+        lens = [400, 350, 800, 330, 20, 1500, 321]
+        shared = [1, 2, 3, 5, 6]
+        lone = []
     elif name == "odd-37-two-layers":
         P, layers, H = 37, 2, 32
         lens = [600, 593, 1000, 4000, 40, 2600, 900, 1200, 600, 601, 3000, 7]
@@ -92,7 +97,7 @@ def _case(name):
     return b, marks, P
 
 
-CASES = ["ragged-125", "aligned-3-tiles", "one-block", "odd-37-two-layers"]
+CASES = ["ragged-125", "aligned-3-tiles", "one-block", "heads-12", "odd-37-two-layers"]
 
 
 @pytest.mark.parametrize("name", CASES)
