@@ -43,6 +43,8 @@ PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_chunk512_hbm_counters
 PREFILL_SOURCES = [os.path.join(CSRC, n) for n in ("prefill.hip", "decode_core.h", "device_common.h")]
 APPEND_COUNTERS = os.path.join(ROOT, "profiles", "append_bulk_hbm_counters.json")
 APPEND_SOURCES = [os.path.join(CSRC, n) for n in ("append.hip", "device_common.h")]
+FP8_GQA_COUNTERS = os.path.join(ROOT, "profiles", "fp8_gqa_decode_average_mix_hbm_counters.json")
+FP8_SOURCES = [os.path.join(CSRC, n) for n in ("fp8.hip", "decode_core.h", "device_common.h")]
 
 
 def source_digest(sources=None) -> str:
@@ -66,6 +68,19 @@ def counted_record(path, sources):
     if rec.get("source_sha256") != source_digest(sources):
         return None
     return rec
+
+
+def fp8_gqa_traffic(kind):
+    """HBM bytes per 8-bit ("fp8") or grouped-query ("gqa") decode launch from
+    the committed counter summary, or None when its sources have changed."""
+    try:
+        with open(FP8_GQA_COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get(f"source_sha256_{kind}") != source_digest(FP8_SOURCES if kind == "fp8" else DECODE_SOURCES):
+        return None
+    return rec.get(f"{kind}_traffic_bytes_per_launch")
 
 
 def counted_traffic():
@@ -508,6 +523,7 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
         "kv_tokens_per_s": tokens / (ms / 1e3),
         "hbm_tb_s": kv_bytes / (ms / 1e3) / 1e12,
         "hbm_frac_of_peak": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "traffic_bytes_per_launch": fp8_gqa_traffic("gqa"),
     }
 
 
@@ -595,6 +611,7 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
         "decode_avg_launch_us": launch_ms * 1e3,
         "decode_hbm_tb_s": layer_bytes / (launch_ms / 1e3) / 1e12,
         "decode_frac_of_peak": layer_bytes / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "decode_traffic_bytes_per_launch": fp8_gqa_traffic("fp8"),
     }
 
 
