@@ -142,6 +142,18 @@ def _dptr(t, what: str, dtype_bytes: int | None = None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _rows_need(rows: int, heads: int, **tensors):
+    for what, t in tensors.items():
+        _need(t, rows * heads * HEAD_DIM, what)
+
+
+def _need(t, n: int, what: str):
+    """The kernels index these arrays by the call's counts; a shorter tensor
+    would be read or written past its end, so it is refused here."""
+    if t is not None and int(t.numel()) < int(n):
+        raise ValueError(f"{what} has {int(t.numel())} elements, the call needs {int(n)}")
+
+
 class PagedCache:
     """Descriptor of a caller-owned device KV pool tensor
     [num_blocks, num_layers, 2, num_heads, 16, 128] of FP16 (or its uint16 bits)."""
@@ -162,6 +174,8 @@ class PagedCache:
 def append(cache: PagedCache, layer: int, k_new, v_new, positions, request_of_token, block_tables, stream=None):
     T = int(positions.numel())
     R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(T, cache.num_heads, k_new=k_new, v_new=v_new)
+    _need(request_of_token, T, "request_of_token")
     _check(lib().pkv_append(ctypes.byref(cache.desc), int(layer), _dptr(k_new, "k_new", 2), _dptr(v_new, "v_new", 2),
                             _dptr(positions, "positions", 4), _dptr(request_of_token, "request_of_token", 4), T,
                             _dptr(block_tables, "block_tables", 4), R, stride, _stream_ptr(stream)))
@@ -185,6 +199,8 @@ def decode_attention(cache: PagedCache, layer: int, out, q, block_tables, contex
 def decode_attention_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q, block_tables, context_lens,
                          max_context_len: int, scale: float, workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(R, num_q_heads, out=out, q=q)
+    _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_decode_attention_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(layer), _dptr(out, "out", 2),
                                           _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,
@@ -202,6 +218,9 @@ def decode_attention_append(cache: PagedCache, layer: int, out, q, k_new, v_new,
 def decode_attention_append_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q, k_new, v_new, block_tables,
                                 context_lens, max_context_len: int, scale: float, workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(R, num_q_heads, out=out, q=q)
+    _rows_need(R, cache.num_heads, k_new=k_new, v_new=v_new)
+    _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_decode_attention_append_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(layer),
                                                  _dptr(out, "out", 2), _dptr(q, "q", 2), _dptr(k_new, "k_new", 2),
@@ -221,6 +240,9 @@ def decode_attention_prefix(cache: PagedCache, layer: int, out, q, block_tables,
     """Decode attention that reads a shared prefix of `prefix_blocks` blocks once
     for every row marked in `shares_prefix` (device int32 [rows])."""
     R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(R, cache.num_heads, out=out, q=q)
+    _need(context_lens, R, "context_lens")
+    _need(shares_prefix, R, "shares_prefix")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_decode_attention_prefix(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2),
                                              _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,
@@ -252,6 +274,9 @@ def chunked_prefill_attention_gqa(cache: PagedCache, num_q_heads: int, layer: in
                                   workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)
     T = int(q.shape[0])
+    _rows_need(T, num_q_heads, out=out, q=q)
+    _need(query_start, R + 1, "query_start")
+    _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_chunked_prefill_attention_gqa(
         ctypes.byref(cache.desc), int(num_q_heads), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2),
@@ -330,6 +355,8 @@ def append_fp8(cache: PagedCache8, layer: int, k_new, v_new, positions, request_
                stream=None):
     T = int(positions.numel())
     R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(T, cache.num_heads, k_new=k_new, v_new=v_new)
+    _need(request_of_token, T, "request_of_token")
     _check(lib().pkv_append_fp8(ctypes.byref(cache.desc), int(layer), _dptr(k_new, "k_new", 2),
                                 _dptr(v_new, "v_new", 2), _dptr(positions, "positions", 4),
                                 _dptr(request_of_token, "request_of_token", 4), T,
@@ -344,6 +371,8 @@ def decode_attention_append_fp8(cache: PagedCache8, layer: int, out, q, k_new, v
                                 max_context_len: int, scale: float, workspace=None, stream=None):
     """Quantize and append each row's new token at position context_lens[r] - 1, then decode (one fused launch)."""
     R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(R, cache.num_heads, out=out, q=q, k_new=k_new, v_new=v_new)
+    _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_decode_attention_append_fp8(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2),
                                                  _dptr(q, "q", 2), _dptr(k_new, "k_new", 2), _dptr(v_new, "v_new", 2),
@@ -356,6 +385,8 @@ def decode_attention_append_fp8(cache: PagedCache8, layer: int, out, q, k_new, v
 def decode_attention_fp8(cache: PagedCache8, layer: int, out, q, block_tables, context_lens, max_context_len: int,
                          scale: float, workspace=None, stream=None):
     R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(R, cache.num_heads, out=out, q=q)
+    _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_decode_attention_fp8(ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2),
                                           _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,

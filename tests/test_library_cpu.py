@@ -281,3 +281,44 @@ def test_validation_appending_decodes():
                                              16, FAKE, 4, 256, 0.088, FAKE, 1 << 20, None) == -1
     assert L.pkv_decode_attention_append_fp8(ctypes.byref(d8), 1, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 256,
                                              0.088, FAKE, 1 << 20, None) == -1
+
+
+def test_binding_refuses_short_tensors():
+    """The binding checks each tensor against the counts the call will index it
+    by (rows x heads x 128 for queries and outputs, rows for lengths), before
+    any library call: a short tensor would be read or written past its end."""
+    torch = pytest.importorskip("torch")
+
+    class Cache:  # only the head count is consulted before the refusal
+        num_heads = 8
+        desc = None
+
+    R, H = 4, 8
+    tables = torch.zeros((R, 16), dtype=torch.int32)
+    lens = torch.ones(R, dtype=torch.int32)
+    full = torch.zeros((R, H, 128), dtype=torch.float16)
+    short = torch.zeros((R - 1, H, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="out has"):
+        pkv.decode_attention_gqa(Cache(), H, 0, short, full, tables, lens, 64, 0.088)
+    with pytest.raises(ValueError, match="q has"):
+        pkv.decode_attention_gqa(Cache(), H, 0, full, short, tables, lens, 64, 0.088)
+    with pytest.raises(ValueError, match="context_lens has"):
+        pkv.decode_attention_gqa(Cache(), H, 0, full, full, tables, lens[:2], 64, 0.088)
+    with pytest.raises(ValueError, match="out has"):  # 4 query heads per KV head need 4x the output rows
+        pkv.decode_attention_gqa(Cache(), 4 * H, 0, full, full, tables, lens, 64, 0.088)
+    with pytest.raises(ValueError, match="k_new has"):
+        pkv.decode_attention_append(Cache(), 0, full, full, short, full, tables, lens, 64, 0.088)
+    with pytest.raises(ValueError, match="shares_prefix has"):
+        pkv.decode_attention_prefix(Cache(), 0, full, full, tables, lens, 64, 0.088, lens[:1], 2)
+    pos = torch.zeros(R, dtype=torch.int32)
+    with pytest.raises(ValueError, match="v_new has"):
+        pkv.append(Cache(), 0, full, short, pos, pos, tables)
+    with pytest.raises(ValueError, match="request_of_token has"):
+        pkv.append(Cache(), 0, full, full, pos, pos[:1], tables)
+    qs = torch.tensor([0, 1, 2, 3, 4], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out has"):
+        pkv.chunked_prefill_attention(Cache(), 0, short, full, qs, tables, lens, 1, 64, 0.088)
+    with pytest.raises(ValueError, match="query_start has"):
+        pkv.chunked_prefill_attention(Cache(), 0, full, full, qs[:R], tables, lens, 1, 64, 0.088)
+    with pytest.raises(ValueError, match="out has"):
+        pkv.decode_attention_fp8(Cache(), 0, short, full, tables, lens, 64, 0.088)
