@@ -132,7 +132,7 @@ def _prefill(torch, pool, Hq, q, b):
     return out
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_gqa_prefill_parity_and_duplicated_heads(G):
     torch = torch_cuda()
     Hkv = 8
