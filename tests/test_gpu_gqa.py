@@ -64,6 +64,22 @@ def test_gqa_decode_parity(G):
         assert_close(host_f64(got), ref, f"G={G} layer {layer}")
 
 
+def test_gqa_decode_odd_kv_heads():
+    """3 KV heads of 4 query heads each: 12 query heads, a merge grid of three
+    4-head groups."""
+    torch = torch_cuda()
+    G, Hkv = 4, 3
+    Hq = Hkv * G
+    lens = [1, 17, 256, 257, 1300]
+    b = build_batch("gqa-odd", 47, lens, [1] * len(lens), num_blocks=130, num_layers=1, num_heads=Hkv, stride=90)
+    q = _queries(57, len(lens), Hq)
+    pool = _full_pool(b)
+    say(f"gqa decode G={G} Hkv={Hkv}")
+    got = _decode(torch, pool, Hq, 0, q, b.block_tables, b.context_lens)
+    ref = opaged.decode(pool[:, 0], q, b.block_tables, b.context_lens, SCALE, group=G)
+    assert_close(host_f64(got), ref, f"G={G} Hkv={Hkv}")
+
+
 def test_gqa_decode_beyond_64_ranges():
     """Grouped decode (G = 4) over rows of 79 and 65 ranges: the merge takes its
     ranges in several passes of 64."""
