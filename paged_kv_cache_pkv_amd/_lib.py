@@ -84,9 +84,15 @@ SIGNATURES = {
 _lib = None
 
 
-def load(path: str | None = None):
+POOL_SYMBOLS = ("pkv_last_error", "pkv_version", "pkv_pool_create", "pkv_pool_create_from_list", "pkv_pool_destroy",
+                "pkv_alloc", "pkv_ref", "pkv_free", "pkv_grow", "pkv_num_free", "pkv_num_blocks", "pkv_ref_count",
+                "pkv_free_list", "pkv_blocks_needed")
+
+
+def load(path: str | None = None, names=None):
     """Load libpkv.so once.  Raises if it has not been built: there is no
-    fallback implementation."""
+    fallback implementation.  `path` and `names` load another build of the
+    library (e.g. the sanitized host pool, with names=POOL_SYMBOLS)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
@@ -94,7 +100,8 @@ def load(path: str | None = None):
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing; build it with `python -m paged_kv_cache_pkv_amd.build`")
     lib = ctypes.CDLL(p)
-    for name, (res, args) in SIGNATURES.items():
+    for name in (names or SIGNATURES):
+        res, args = SIGNATURES[name]
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args

@@ -21,8 +21,7 @@ SOURCES = ["errors.cpp", "pool.cpp", "append.hip", "decode.hip", "prefill.hip", 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU forms are kept out of the generated code.
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc() -> str:
@@ -60,6 +59,24 @@ def build(verbose: bool = False) -> str:
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+POOL_SANITIZED = os.path.join(ROOT, "_build", "libpkv_pool_sanitized.so")
+
+
+def build_pool_sanitized(verbose: bool = False) -> str:
+    """The host block pool alone (pool.cpp, errors.cpp), built with g++ under
+    AddressSanitizer and UndefinedBehaviorSanitizer into a test-only library.
+    It holds the pool's symbols and no device code; tests load it into a
+    process that preloads the sanitizer runtimes."""
+    os.makedirs(os.path.dirname(POOL_SANITIZED), exist_ok=True)
+    srcs = [os.path.join(CSRC, s) for s in ("errors.cpp", "pool.cpp")]
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", f"-I{INCLUDE}", f"-I{CSRC}", *srcs,
+           "-o", POOL_SANITIZED + ".tmp"]
+    _run(cmd, verbose)
+    os.replace(POOL_SANITIZED + ".tmp", POOL_SANITIZED)
+    return POOL_SANITIZED
 
 
 if __name__ == "__main__":

@@ -9,7 +9,14 @@ thread_local std::string g_last_error;
 }
 
 namespace pkv {
-void set_error(const std::string& msg) { g_last_error = msg; }
+// A message that cannot be stored (no host memory) leaves the previous one;
+// the status code still reports the failure.
+void set_error(const std::string& msg) {
+  try {
+    g_last_error = msg;
+  } catch (...) {
+  }
+}
 void clear_error() { g_last_error.clear(); }
 }  // namespace pkv
 

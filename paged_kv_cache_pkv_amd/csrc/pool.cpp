@@ -44,8 +44,16 @@ int create(int32_t num_blocks, const int32_t* free_ids, int32_t n_free, pkv_pool
   if (num_blocks < 1) return pkv::fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
   pkv_pool* p = new (std::nothrow) pkv_pool;
   if (!p) return pkv::fail(PKV_ERR_INVALID_ARG, "out of host memory");
-  p->refs.assign(static_cast<size_t>(num_blocks), 0);
-  p->scratch.assign(static_cast<size_t>(num_blocks), 0);
+  // Every allocation the pool will ever make happens here: the free stack is
+  // reserved at its largest size, so a later release never reallocates it.
+  try {
+    p->refs.assign(static_cast<size_t>(num_blocks), 0);
+    p->scratch.assign(static_cast<size_t>(num_blocks), 0);
+    p->free_stack.reserve(static_cast<size_t>(num_blocks));
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return pkv::fail(PKV_ERR_INVALID_ARG, "out of host memory");
+  }
   if (free_ids == nullptr) {
     p->free_stack.resize(static_cast<size_t>(num_blocks));
     for (int32_t i = 0; i < num_blocks; ++i) p->free_stack[i] = i;
