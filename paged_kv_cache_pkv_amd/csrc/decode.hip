@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_ke
   const int h = __builtin_amdgcn_readfirstlane(hg * kWavesPerGroup + (threadIdx.x >> 6));
   if (h >= a.num_heads) return;
 
-  int L = a.context_lens[r];
-  L = L > a.max_context_len ? a.max_context_len : L;
+  const int L_in = a.context_lens[r];
+  const int L = L_in > a.max_context_len ? a.max_context_len : L_in;
   const size_t rh = (size_t)r * a.num_heads + h;
   if (L < 1) {
     if (split == 0 && (threadIdx.x & 63) < 16) a.out[rh * 16 + (threadIdx.x & 15)] = make_uint4(0u, 0u, 0u, 0u);
@@ -94,7 +94,9 @@ __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_ke
   }
   if (split >= decode_splits(L)) return;
   const size_t slot = rh * a.max_splits + split;
-  if constexpr (kAppend)
+  // A row longer than max_context_len is read clamped, for memory safety, but
+  // its new token's slot lies past the clamp: it appends nothing.
+  if (kAppend && L_in == L)
     decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
                  a.block_tables + (size_t)r * a.bt_stride, L, split, a.q + rh * 16, a.qk_scale, a.out + rh * 16,
                  a.part_o + slot * kHeadDim, a.part_ml + slot, a.k_new + rh * 16, a.v_new + rh * 16);
@@ -140,8 +142,8 @@ __global__ __launch_bounds__(kGqaThreads) void decode_gqa_kernel(DecodeArgs a) {
   if (r >= a.num_rows) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  int L = a.context_lens[r];
-  L = L > a.max_context_len ? a.max_context_len : L;
+  const int L_in = a.context_lens[r];
+  const int L = L_in > a.max_context_len ? a.max_context_len : L_in;
   const size_t rh = (size_t)r * a.num_q_heads + (size_t)h * G;  // the KV head's first query head
   if (L < 1) {
     if (split == 0 && wave == 0 && lane < 16)
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(kGqaThreads) void decode_gqa_kernel(DecodeArgs a) {
   const uint4* new_k = nullptr;
   const uint4* new_v = nullptr;
   if constexpr (kAppend) {
-    if (b0 < b1 && b1 == nb) {
+    // a row clamped to max_context_len appends nothing (its slot lies past the clamp)
+    if (b0 < b1 && b1 == nb && L_in == L) {
       new_k = a.k_new + ((size_t)r * a.num_heads + h) * 16;
       new_v = a.v_new + ((size_t)r * a.num_heads + h) * 16;
     }

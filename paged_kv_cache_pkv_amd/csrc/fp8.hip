@@ -2,7 +2,7 @@
 //
 // An 8-bit cache halves the bytes of every cached token and the attention
 // read traffic, at a quality cost that grows with context length (Inference
-// Infrastructure, seeitflow.com, "KV-cache precision"; The inference engine,
+// Infrastructure, seeitflow.com, its paragraph on KV-cache precision; The inference engine,
 // wpnews.pro, "IO-aware attention and quantization attack different costs").
 // Codes are FP8 E4M3 (the OCP format gfx950 converts natively), with one fp32
 // scale per (token, head) row of 128 values: s = amax / 448 and codes encode
@@ -271,8 +271,8 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
-  int L = a.context_lens[r];
-  L = L > a.max_context_len ? a.max_context_len : L;
+  const int L_in = a.context_lens[r];
+  const int L = L_in > a.max_context_len ? a.max_context_len : L_in;
   const int lane = threadIdx.x & 63;
   const int group = lane >> 4;
   const int chunk = lane & 15;
@@ -296,7 +296,8 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
   for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
 
   // the new token (slot ns of the last block: group ns / 4, entry ns % 4)
-  const bool takes_new = kAppend && split == nsplit - 1;
+  // a row clamped to max_context_len appends nothing (its slot lies past the clamp)
+  const bool takes_new = kAppend && split == nsplit - 1 && L_in == L;
   const int ns = (L - 1) & (kBlockSize - 1);
   u32x2 nkc = u32x2{0u, 0u}, nvc = nkc;
   float nks = 0.0f, nvs = 0.0f;
