@@ -30,8 +30,9 @@
  *    every block id against num_blocks and every table index against
  *    bt_stride, so a bad entry yields unspecified values for that row (or an
  *    append that is skipped) but never an out-of-bounds memory access.
- *  - The block pool object is single-owner and not thread-safe: one scheduler
- *    thread owns it (faangrind: "One scheduler thread owns the GPU").
+ *  - The block pool object is single-owner and not thread-safe: a single
+ *    scheduler thread drives the GPU and holds it (LLM inference batching,
+ *    faangrind, scheduler step 3).
  */
 #ifndef PKV_H
 #define PKV_H
@@ -66,8 +67,8 @@ const char* pkv_version(void);
  * pushes them back in the order given (scalablesystem.dev BlockManager;
  * Serving LLMs, sreshtalluri.github.io: "Paged KV memory" BlockPool).
  * A block's count is 1 after allocation, +1 per share, -1 per release; it
- * returns to the free list only at 0 (faangrind data model: "ref_count ...
- * above 1 when n samples share one prompt"; failure list: a block freed
+ * returns to the free list only at 0 (faangrind data model: ref_count exceeds
+ * 1 while several samples share one prompt; failure list: a block freed
  * while still referenced leaks one user's text into another's answer).
  * Every call validates all of its ids before changing anything.
  * ---------------------------------------------------------------------- */
@@ -87,8 +88,8 @@ void pkv_pool_destroy(pkv_pool* pool);
 
 /* Pop n ids into out_ids[0..n) (out_ids[0] = old top), each with count 1.
  * All or nothing: with fewer than n free, returns PKV_ERR_OUT_OF_BLOCKS and
- * changes nothing (Serving LLMs, BlockPool.grow: "False means: preempt
- * someone"). */
+ * changes nothing (Serving LLMs, "Paged KV memory": BlockPool.grow reports the
+ * shortfall so that the scheduler preempts a sequence). */
 int pkv_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids);
 
 /* Count +1 for each listed id (a new sharer of a prefix block).  Every id must
@@ -141,8 +142,8 @@ typedef struct pkv_cache {
  * KV append.
  *
  * For each new token t < num_tokens of one step (the step's flat token list
- * tagged by request, faangrind "One step with B decode rows and a prefill
- * chunk"): row r = request_of_token[t], position p = positions[t],
+ * tagged by request, faangrind data model: the step tensors positions and
+ * request_of_token): row r = request_of_token[t], position p = positions[t],
  * block b = block_tables[r * bt_stride + p / 16], slot s = p % 16; copies the
  * bits of k_new[t] into pool[b][layer][0][:][s][:] and of v_new[t] into
  * pool[b][layer][1][:][s][:].  A row takes a new block every 16 tokens
@@ -206,7 +207,8 @@ int32_t pkv_split_tokens(void);
  * (faangrind scheduler step 7: each decode row appends its token, then
  * attends).  Same contract and workspace as pkv_decode_attention; the
  * appended slot must not be in a shared block.  Rows with context_lens[r] < 1
- * append nothing. */
+ * or context_lens[r] > max_context_len break the length contract: they append
+ * nothing (no pool byte changes for them) and their output is unspecified. */
 int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer, void* out, const void* q, const void* k_new,
                                 const void* v_new, const int32_t* block_tables, int32_t bt_stride,
                                 const int32_t* context_lens, int32_t num_rows, int32_t max_context_len, float scale,
@@ -220,8 +222,9 @@ int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer, void* out
  * query_start[r] positions of its context, L_r - n_r .. L_r - 1 with
  * L_r = context_lens[r], and their keys and values were appended before the
  * call.  Query i of the row sits at p = L_r - n_r + i and attends causally to
- * keys 0..p (The inference engine, wpnews.pro: prefill "respects the causal
- * mask").  Rows with n_r == 1 are decode rows; a prefill chunk and decode rows
+ * keys 0..p (The inference engine, wpnews.pro, "Prefill and decode ask the
+ * accelerator for different work": prefill attention is causal).  Rows with
+ * n_r == 1 are decode rows; a prefill chunk and decode rows
  * share the step as a flat list of request-tagged tokens (faangrind "Prefill
  * and decode share each step").  The chunk's QK^T and PV products run on
  * MFMA matrix cores in FP16 with fp32 accumulation.
@@ -371,7 +374,8 @@ int pkv_swap_in(const pkv_cache* cache, const void* host_src, const int32_t* ids
  *
  * An 8-bit cache halves the bytes of every cached token and the attention
  * read traffic, with a quality risk that grows with context length
- * (Inference Infrastructure, seeitflow.com, "KV-cache precision"; The
+ * (Inference Infrastructure, seeitflow.com, its paragraph on KV-cache
+ * precision; The
  * inference engine, wpnews.pro, "IO-aware attention and quantization attack
  * different costs").  Codes are FP8 E4M3 (OCP format: bias 7, three mantissa
  * bits, largest finite 448, 0x7F NaN) with one fp32 scale per (token, head)
@@ -413,7 +417,8 @@ int pkv_decode_attention_fp8(const pkv_cache8* cache, int32_t layer, void* out, 
  * quantized and written at position context_lens[r] - 1 exactly as
  * pkv_append_fp8 would, and the result is pkv_decode_attention_fp8's: the
  * same codes, scales and output bits as those two calls in sequence, in one
- * launch fewer. */
+ * launch fewer.  As in pkv_decode_attention_append, a row whose length lies
+ * outside [1, max_context_len] appends nothing. */
 int pkv_decode_attention_append_fp8(const pkv_cache8* cache, int32_t layer, void* out, const void* q,
                                     const void* k_new, const void* v_new, const int32_t* block_tables,
                                     int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
