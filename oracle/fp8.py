@@ -4,20 +4,21 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 An 8-bit cache halves the bytes of every cached token and so the attention
 read traffic, with a quality risk that grows with context length (Inference
-Infrastructure, seeitflow.com, "KV-cache precision"; The inference engine,
+Infrastructure, seeitflow.com, its paragraph on KV-cache precision; The inference engine,
 wpnews.pro, "IO-aware attention and quantization attack different costs":
 KV quantization changes bytes per token but adds accuracy questions).  The
-pages fix no format; this oracle follows the one the library uses:
+pages fix no format; the reading taken (one fp32 scale per row of 128 values,
+E4M3 codes) is written out here by its definition:
 
 * Codes are FP8 E4M3 ("E4M3FN" of the OCP 8-bit floating point format): one
   sign bit, four exponent bits with bias 7, three mantissa bits; exponent 0 is
   subnormal (m / 8 * 2^-6), code 0x7F / 0xFF is NaN and there is no infinity,
   so the largest finite magnitude is 1.75 * 2^8 = 448.
 * Every (token, head) row of 128 values x gets the scale s = amax / 448 with
-  amax = max |x|; codes encode x * (448 / amax), rounded to the nearest code
-  (ties to the even mantissa) and saturated at 448.  A zero row has s = 0 and
-  all-zero codes.  All of this is fp32 arithmetic, so the library computes the
-  same bits.
+  amax = max |x|; the code of x is the finite E4M3 value nearest to
+  x * (448 / amax) (that product taken in fp32), a tie between two neighbours
+  going to the one with the even mantissa, and magnitudes above 448 saturating
+  to 448.  A zero row has s = 0 and all-zero codes.
 * A cached value reads back as decode(code) * s.
 
 Pool arrays: codes [num_blocks, layers, 2, heads, 16, head_dim] uint8 and
@@ -50,27 +51,23 @@ def decode_table() -> np.ndarray:
 
 
 def encode(x) -> np.ndarray:
-    """Nearest E4M3 code of float32 values (ties to the even mantissa),
-    magnitudes of 448 and above saturated to 448.  Returns uint8."""
+    """E4M3 code of each float32 value, by the definition: the finite value of
+    the format nearest to |x| (the 127 non-negative codes 0x00..0x7E, whose
+    values increase with the code), a tie between two neighbours going to the
+    even code (the code's low bit is the mantissa's last bit), magnitudes above
+    448 saturating to 448 (0x7E); the sign bit is x's.  Returns uint8."""
     x = np.asarray(x, dtype=np.float32)
-    sign = np.signbit(x).astype(np.uint8) << 7
-    a = np.abs(x).astype(np.float32)
-    code = np.zeros(x.shape, dtype=np.int32)
-    sat = a >= np.float32(FP8_MAX)
-    sub = a < np.float32(2.0 ** -6)
-    # subnormal range: multiples of 2^-9
-    q_sub = np.rint(a * np.float32(512.0)).astype(np.int32)  # 0..8; 8 is the smallest normal, code 0x08
-    # normal range: a = 2^e * (1 + f), f in [0, 1); three mantissa bits
-    mant, ex = np.frexp(a)  # a = mant * 2^ex, mant in [0.5, 1)
-    e = ex.astype(np.int32) - 1
-    f = (np.ldexp(a, -e) - np.float32(1.0)).astype(np.float32)
-    m = np.rint(f * np.float32(8.0)).astype(np.int32)
-    carry = m == 8
-    m = np.where(carry, 0, m)
-    e = np.where(carry, e + 1, e)
-    q_norm = ((e + 7) << 3) | m
-    code = np.where(sub, q_sub, q_norm)
-    code = np.where(sat, 0x7E, code)
+    sign = (np.signbit(x).astype(np.uint8) << 7).astype(np.uint8)
+    a = np.abs(x).astype(np.float64)  # exact: float32 values are float64 values
+    vals = decode_table()[:0x7F]      # non-negative finite values, increasing with the code
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 1, 0x7E)  # vals[hi-1] < a <= vals[hi], clipped
+    lo = hi - 1
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= FP8_MAX, 0x7E, code)  # saturation (also the clipped search past 448)
+    code = np.where(a <= vals[0], 0, code)     # zero
     return (code.astype(np.uint8) | sign).astype(np.uint8)
 
 

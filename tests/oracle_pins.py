@@ -438,8 +438,18 @@ def pin_fp8_format(seed=20):
     assert enc(1000.0) == 0x7E and enc(-1e6) == 0xFE and enc(464.0) == 0x7E  # saturation
     finite = np.array([c for c in range(256) if not np.isnan(t[c])])
     assert np.array_equal(ofp8.encode(t[finite].astype(np.float32)), finite.astype(np.uint8))
-    # brute force: the nearest finite code, ties to the even code
+    # an independent implementation: torch's CPU conversion to float8_e4m3fn
+    # rounds to nearest even and agrees with the definition below 464 (above
+    # that it gives NaN where the reading saturates)
+    import torch
     rng = np.random.default_rng(seed)
+    xs = np.concatenate([rng.uniform(-463, 463, 20000), rng.uniform(-0.05, 0.05, 20000),
+                         rng.standard_normal(20000) * 8, (t[finite][:-1] + t[finite][1:]) / 2,
+                         np.nextafter((t[finite][:-1] + t[finite][1:]) / 2, 0)]).astype(np.float32)
+    xs = xs[np.abs(xs) < 464]
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ofp8.encode(xs), ref)
+    # brute force: the nearest finite code, ties to the even code
     xs = np.concatenate([rng.uniform(-460, 460, 3000), rng.uniform(-0.03, 0.03, 3000),
                          (t[finite][:-1] + t[finite][1:]) / 2]).astype(np.float32)
     vals = t[finite]
