@@ -202,10 +202,13 @@ def decode_attention_gqa(cache: PagedCache, num_q_heads: int, layer: int, out, q
     _rows_need(R, num_q_heads, out=out, q=q)
     _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_decode_attention_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(layer), _dptr(out, "out", 2),
-                                          _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,
-                                          _dptr(context_lens, "context_lens", 4), R, int(max_context_len),
-                                          float(scale), _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+    args = (int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2), _dptr(block_tables, "block_tables", 4), stride,
+            _dptr(context_lens, "context_lens", 4), R, int(max_context_len), float(scale),
+            _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream))
+    if int(num_q_heads) == cache.num_heads:  # one query head per KV head: the plain call
+        _check(lib().pkv_decode_attention(ctypes.byref(cache.desc), *args))
+    else:
+        _check(lib().pkv_decode_attention_gqa(ctypes.byref(cache.desc), int(num_q_heads), *args))
 
 
 def decode_attention_append(cache: PagedCache, layer: int, out, q, k_new, v_new, block_tables, context_lens,
@@ -222,12 +225,13 @@ def decode_attention_append_gqa(cache: PagedCache, num_q_heads: int, layer: int,
     _rows_need(R, cache.num_heads, k_new=k_new, v_new=v_new)
     _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_decode_attention_append_gqa(ctypes.byref(cache.desc), int(num_q_heads), int(layer),
-                                                 _dptr(out, "out", 2), _dptr(q, "q", 2), _dptr(k_new, "k_new", 2),
-                                                 _dptr(v_new, "v_new", 2), _dptr(block_tables, "block_tables", 4),
-                                                 stride, _dptr(context_lens, "context_lens", 4), R,
-                                                 int(max_context_len), float(scale), _dptr(workspace, "workspace"),
-                                                 ws_bytes, _stream_ptr(stream)))
+    args = (int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2), _dptr(k_new, "k_new", 2), _dptr(v_new, "v_new", 2),
+            _dptr(block_tables, "block_tables", 4), stride, _dptr(context_lens, "context_lens", 4), R,
+            int(max_context_len), float(scale), _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream))
+    if int(num_q_heads) == cache.num_heads:  # one query head per KV head: the plain call
+        _check(lib().pkv_decode_attention_append(ctypes.byref(cache.desc), *args))
+    else:
+        _check(lib().pkv_decode_attention_append_gqa(ctypes.byref(cache.desc), int(num_q_heads), *args))
 
 
 def decode_workspace_size_prefix(cache: PagedCache, num_rows: int, max_context_len: int, prefix_blocks: int) -> int:
@@ -254,7 +258,8 @@ def decode_attention_prefix(cache: PagedCache, layer: int, out, q, block_tables,
 
 def prefill_workspace_size(cache: PagedCache, num_rows: int, total_q: int, max_q_per_row: int,
                            max_context_len: int) -> int:
-    return prefill_workspace_size_gqa(cache, cache.num_heads, num_rows, total_q, max_q_per_row, max_context_len)
+    return int(lib().pkv_prefill_workspace_size(ctypes.byref(cache.desc), int(num_rows), int(total_q),
+                                                int(max_q_per_row), int(max_context_len)))
 
 
 def prefill_workspace_size_gqa(cache: PagedCache, num_q_heads: int, num_rows: int, total_q: int, max_q_per_row: int,
@@ -278,11 +283,14 @@ def chunked_prefill_attention_gqa(cache: PagedCache, num_q_heads: int, layer: in
     _need(query_start, R + 1, "query_start")
     _need(context_lens, R, "context_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_chunked_prefill_attention_gqa(
-        ctypes.byref(cache.desc), int(num_q_heads), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2),
-        _dptr(query_start, "query_start", 4), _dptr(block_tables, "block_tables", 4), stride,
-        _dptr(context_lens, "context_lens", 4), R, T, int(max_q_per_row), int(max_context_len), float(scale),
-        _dptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+    args = (int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2), _dptr(query_start, "query_start", 4),
+            _dptr(block_tables, "block_tables", 4), stride, _dptr(context_lens, "context_lens", 4), R, T,
+            int(max_q_per_row), int(max_context_len), float(scale), _dptr(workspace, "workspace"), ws_bytes,
+            _stream_ptr(stream))
+    if int(num_q_heads) == cache.num_heads:  # one query head per KV head: the plain call
+        _check(lib().pkv_chunked_prefill_attention(ctypes.byref(cache.desc), *args))
+    else:
+        _check(lib().pkv_chunked_prefill_attention_gqa(ctypes.byref(cache.desc), int(num_q_heads), *args))
 
 
 # ------------------------------------------------------------------ whole blocks

@@ -322,3 +322,44 @@ def test_binding_refuses_short_tensors():
         pkv.chunked_prefill_attention(Cache(), 0, full, full, qs[:R], tables, lens, 1, 64, 0.088)
     with pytest.raises(ValueError, match="out has"):
         pkv.decode_attention_fp8(Cache(), 0, short, full, tables, lens, 64, 0.088)
+
+
+def test_validation_chunked_prefill_args():
+    """pkv_chunked_prefill_attention checks every scalar, pointer, alignment
+    and workspace before it launches anything; its workspace size is the one
+    of the grouped call with one query head per KV head."""
+    L = pkv.lib()
+    d = _desc()
+
+    def call(layer=0, out=FAKE, q=FAKE, qs=FAKE, bt=FAKE, stride=16, cl=FAKE, R=4, T=40, maxq=32, maxL=256,
+             scale=0.088, ws=FAKE, wsb=1 << 24, desc=None):
+        return L.pkv_chunked_prefill_attention(ctypes.byref(desc or d), layer, out, q, qs, bt, stride, cl, R, T, maxq,
+                                               maxL, scale, ws, wsb, None)
+    need = L.pkv_prefill_workspace_size(ctypes.byref(d), 4, 40, 32, 256)
+    assert need > 0
+    assert need == L.pkv_prefill_workspace_size_gqa(ctypes.byref(d), 32, 4, 40, 32, 256)
+    assert L.pkv_prefill_workspace_size(ctypes.byref(d), 4, 0, 32, 256) == 0
+    assert L.pkv_prefill_workspace_size(None, 4, 40, 32, 256) == 0
+    assert L.pkv_chunked_prefill_attention(None, 0, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, 40, 32, 256, 0.088, FAKE,
+                                           1 << 24, None) == -1
+    assert call(desc=_desc(head_dim=64)) == -2
+    assert call(desc=_desc(block_size=8)) == -2
+    assert call(layer=1) == -1 and call(layer=-1) == -1
+    assert call(R=0) == -1
+    assert call(T=0) == -1
+    for k in ("out", "q", "qs", "bt", "cl"):
+        assert call(**{k: None}) == -1, k
+    assert call(stride=0) == -1
+    assert call(maxL=0) == -1
+    assert call(maxL=16 * 16 + 1) == -1                 # beyond the table
+    assert call(maxq=0) == -1
+    assert call(maxq=257) == -1                         # more queries than context
+    assert call(T=20, maxq=32) == -1                    # more queries per row than in the call
+    assert call(scale=float("nan")) == -1 and call(scale=0.0) == -1 and call(scale=float("inf")) == -1
+    assert call(q=ctypes.c_void_p(0x200008)) == -1      # misaligned
+    assert call(out=ctypes.c_void_p(0x200004)) == -1
+    assert call(desc=_desc(base=ctypes.c_void_p(0x100002))) == -1
+    assert call(ws=None) == -6
+    assert call(wsb=need - 1) == -6
+    assert call(ws=ctypes.c_void_p(0x200010), wsb=need) == -6  # 256-byte alignment
+    assert b"workspace" in L.pkv_last_error()
