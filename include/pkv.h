@@ -108,6 +108,18 @@ int pkv_free(pkv_pool* pool, const int32_t* ids, int32_t n);
  * that already covers num_tokens is left as is.  capacity bounds table. */
 int pkv_grow(pkv_pool* pool, int32_t* table, int32_t* table_len, int32_t capacity, int32_t num_tokens);
 
+/* One step's growth for a batch of rows, in one call: row r's table
+ * tables[r * stride .. (r + 1) * stride) is grown as pkv_grow would grow it
+ * to cover num_tokens[r] tokens, rows in order (a row takes a new block every
+ * 16 tokens; faangrind scheduler step 7).  All arguments of every row are
+ * checked first (PKV_ERR_INVALID_ARG, nothing changed).  Each row grows all
+ * or nothing; at the first row the free list cannot cover, the call returns
+ * PKV_ERR_OUT_OF_BLOCKS, that row and those after it unchanged, and the rows
+ * before it grown -- the scheduler then preempts a sequence (Serving LLMs,
+ * "Paged KV memory").  *rows_grown receives the number of rows processed. */
+int pkv_grow_rows(pkv_pool* pool, int32_t* tables, int32_t stride, int32_t* table_lens, const int32_t* num_tokens,
+                  int32_t num_rows, int32_t* rows_grown);
+
 int32_t pkv_num_free(const pkv_pool* pool);
 int32_t pkv_num_blocks(const pkv_pool* pool);
 /* Count of block id, or -1 if id is out of range. */

@@ -103,6 +103,28 @@ class BlockPool:
         _check(lib().pkv_grow(self._h, _iptr(table), ctypes.byref(n), table.size, int(num_tokens)))
         return int(n.value)
 
+    def grow_rows(self, tables: np.ndarray, table_lens: np.ndarray, num_tokens) -> int:
+        """Grow every row r of int32 `tables` [R, stride] (its first table_lens[r]
+        entries in use, updated in place) to cover num_tokens[r] tokens, rows in
+        order, in one library call.  Returns the number of rows grown: R, or the
+        index of the first row the free list could not cover (that row and the
+        later ones are unchanged)."""
+        for a, what in ((tables, "tables"), (table_lens, "table_lens")):
+            if a.dtype != np.int32 or not a.flags.c_contiguous:
+                raise TypeError(f"{what} must be a C-contiguous int32 array")
+        R, stride = tables.shape
+        if table_lens.shape != (R,):
+            raise ValueError("table_lens must hold one length per row")
+        need = _i32(num_tokens)
+        if need.shape != (R,):
+            raise ValueError("num_tokens must hold one count per row")
+        done = ctypes.c_int32(0)
+        rc = lib().pkv_grow_rows(self._h, _iptr(tables), int(stride), _iptr(table_lens), _iptr(need), int(R),
+                                 ctypes.byref(done))
+        if rc != PKV_OK and rc != -3:
+            _check(rc)
+        return int(done.value)
+
     @property
     def num_free(self) -> int:
         return int(lib().pkv_num_free(self._h))

@@ -39,6 +39,7 @@ SIGNATURES = {
     "pkv_ref": (ctypes.c_int, [c_vp, c_i32_p, c_i32]),
     "pkv_free": (ctypes.c_int, [c_vp, c_i32_p, c_i32]),
     "pkv_grow": (ctypes.c_int, [c_vp, c_i32_p, c_i32_p, c_i32, c_i32]),
+    "pkv_grow_rows": (ctypes.c_int, [c_vp, c_i32_p, c_i32, c_i32_p, c_i32_p, c_i32, c_i32_p]),
     "pkv_num_free": (c_i32, [c_vp]),
     "pkv_num_blocks": (c_i32, [c_vp]),
     "pkv_ref_count": (c_i32, [c_vp, c_i32]),
@@ -85,7 +86,7 @@ _lib = None
 
 
 POOL_SYMBOLS = ("pkv_last_error", "pkv_version", "pkv_pool_create", "pkv_pool_create_from_list", "pkv_pool_destroy",
-                "pkv_alloc", "pkv_ref", "pkv_free", "pkv_grow", "pkv_num_free", "pkv_num_blocks", "pkv_ref_count",
+                "pkv_alloc", "pkv_ref", "pkv_free", "pkv_grow", "pkv_grow_rows", "pkv_num_free", "pkv_num_blocks", "pkv_ref_count",
                 "pkv_free_list", "pkv_blocks_needed")
 
 

@@ -165,6 +165,28 @@ int pkv_grow(pkv_pool* p, int32_t* table, int32_t* table_len, int32_t capacity, 
   return PKV_OK;
 }
 
+int pkv_grow_rows(pkv_pool* p, int32_t* tables, int32_t stride, int32_t* table_lens, const int32_t* num_tokens,
+                  int32_t num_rows, int32_t* rows_grown) {
+  if (!p || !rows_grown) return pkv::fail(PKV_ERR_INVALID_ARG, "pool or rows_grown is null");
+  *rows_grown = 0;
+  if (num_rows < 0 || stride < 1) return pkv::fail(PKV_ERR_INVALID_ARG, "need num_rows >= 0 and stride >= 1");
+  if (num_rows > 0 && (!tables || !table_lens || !num_tokens))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "tables, table_lens or num_tokens is null");
+  for (int32_t r = 0; r < num_rows; ++r) {
+    if (num_tokens[r] < 0 || table_lens[r] < 0 || table_lens[r] > stride)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "row " + std::to_string(r) + ": need num_tokens >= 0 and 0 <= table_len <= stride");
+    if (pkv_blocks_needed(num_tokens[r]) > stride)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "row " + std::to_string(r) + ": table stride too small");
+  }
+  for (int32_t r = 0; r < num_rows; ++r) {
+    const int rc = pkv_grow(p, tables + static_cast<size_t>(r) * stride, table_lens + r, stride, num_tokens[r]);
+    if (rc != PKV_OK) return rc;  // OUT_OF_BLOCKS: rows before r keep their growth
+    *rows_grown = r + 1;
+  }
+  pkv::clear_error();
+  return PKV_OK;
+}
+
 int32_t pkv_num_free(const pkv_pool* p) { return p ? static_cast<int32_t>(p->free_stack.size()) : -1; }
 
 int32_t pkv_num_blocks(const pkv_pool* p) { return p ? static_cast<int32_t>(p->refs.size()) : -1; }

@@ -43,15 +43,25 @@ class Row:
     answer: int          # tokens to generate
     generated: int       # tokens generated so far
     shared: int          # leading tokens held in the shared prefix blocks
-    table: np.ndarray    # int32 block ids (capacity = stride)
-    nblk: int            # entries of `table` in use
+    slot: int            # row of the trace's table array this request occupies
+    owner: "ContinuousBatchTrace"
 
     @property
     def length(self) -> int:  # tokens cached before this step's new token
         return self.prompt + self.generated
 
+    @property
+    def table(self) -> np.ndarray:  # int32 block ids (capacity = stride)
+        return self.owner.tables[self.slot]
+
+    @property
+    def nblk(self) -> int:  # entries of `table` in use
+        return int(self.owner.tlen[self.slot])
+
 
 class ContinuousBatchTrace:
+    STAGES = 4  # pinned upload buffers in the ring
+
     def __init__(self, torch, *, seed=3, num_blocks=36864, max_rows=64, prefix_tokens=2000,
                  prompt_range=(50, 8000), answer_range=(1, 1000), heads=32, stride=None, scale=None,
                  device="cuda", shared_decode=False):
@@ -80,7 +90,10 @@ class ContinuousBatchTrace:
         self.next_req = 0
         # the shared prefix: held once by the trace itself so it outlives its rows
         self.prefix_ids = self.pool.alloc(self.prefix_tokens // BLOCK_SIZE)
-        self.rows: list[Row] = []
+        # every row's block table lives in one slot of these arrays
+        self.tables = np.zeros((max_rows, self.stride), dtype=np.int32)
+        self.tlen = np.zeros(max_rows, dtype=np.int32)
+        self.slot_row: list[Row | None] = [None] * max_rows
         self.step_no = 0
         self.max_ctx = max_ctx
         if shared_decode:
@@ -88,7 +101,22 @@ class ContinuousBatchTrace:
         else:
             ws = decode_workspace_size(self.cache, max_rows, max_ctx)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
+        # step metadata: a ring of pinned host buffers, copied asynchronously
+        # into device arrays that every step reuses
+        n_meta = max_rows * self.stride + 3 * max_rows
+        self._stage = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(self.STAGES)]
+        self._stage_done = [None] * self.STAGES
+        self.tab_d = torch.empty((max_rows, self.stride), dtype=torch.int32, device=self.dev)
+        self.lens_d = torch.empty(max_rows, dtype=torch.int32, device=self.dev)
+        self.pos_d = torch.empty(max_rows, dtype=torch.int32, device=self.dev)
+        self.marks_d = torch.empty(max_rows, dtype=torch.int32, device=self.dev)
+        self.rot_d = torch.arange(max_rows, dtype=torch.int32, device=self.dev)
         self.log = {"prefix_ids": self.prefix_ids.copy(), "joins": [], "steps": []}
+
+    @property
+    def rows(self) -> list[Row]:
+        """Running rows in step order (by slot)."""
+        return [r for r in self.slot_row if r is not None]
 
     # ---------------------------------------------------------------- requests
 
@@ -116,9 +144,10 @@ class ContinuousBatchTrace:
         x = torch.randn((3, max(n, 1), self.H, 128), generator=gen, device=self.dev, dtype=torch.float16)
         return x[0, :n].contiguous(), x[1, :n].contiguous(), x[2, :n].contiguous()
 
-    def _join(self, req, prompt, answer):
+    def _join(self, slot, req, prompt, answer):
         torch = self.torch
-        table = np.zeros(self.stride, dtype=np.int32)
+        table = self.tables[slot]
+        table[:] = 0
         shared = self.prefix_tokens if prompt >= self.prefix_tokens else 0
         nblk = 0
         if shared:
@@ -126,8 +155,8 @@ class ContinuousBatchTrace:
             self.pool.ref(self.prefix_ids)
             table[:nshared] = self.prefix_ids
             nblk = nshared
-        nblk = self.pool.grow(table, nblk, prompt)
-        row = Row(req, prompt, answer, 0, shared, table, nblk)
+        self.tlen[slot] = self.pool.grow(table, nblk, prompt)
+        row = Row(req, prompt, answer, 0, shared, slot, self)
         # fill: the private prompt tokens' K/V go into the fresh blocks
         if prompt > shared:
             k, v = self.prompt_kv(req, shared, prompt)
@@ -139,7 +168,9 @@ class ContinuousBatchTrace:
         return row
 
     def _leave(self, row: Row):
-        self.pool.free(row.table[:row.nblk])
+        self.pool.free(self.tables[row.slot, :row.nblk])
+        self.tlen[row.slot] = 0
+        self.slot_row[row.slot] = None
 
     # ---------------------------------------------------------------- one step
 
@@ -147,52 +178,72 @@ class ContinuousBatchTrace:
         """Leave, join, grow, append one token per row, decode.  Returns the
         step's row snapshot (for checkers).  With events=(start, filled,
         launch, end) it records them around the fill of joining rows and
-        around the decode part's launches; the host work in between (table
-        growth, the step's synthetic inputs and their upload) is timed on the
-        host and returned as snap["host_ms"]."""
+        around the decode part's launches.  The host's preparation of the step
+        (one batched table growth through the block pool, and the staging and
+        asynchronous upload of tables, lengths and marks through pinned
+        memory) is timed on the host and returned as snap["host_ms"]; the
+        step's synthetic inputs are drawn before it and not counted."""
         torch = self.torch
-        finished = [r for r in self.rows if r.generated >= r.answer]
-        for r in finished:
-            self._leave(r)
-        self.rows = [r for r in self.rows if r.generated < r.answer]
+        for r in self.rows:
+            if r.generated >= r.answer:
+                self._leave(r)
         if events:
             events[0].record()
-        while len(self.rows) < self.max_rows:
-            self.rows.append(self._join(*self._draw_request()))
+        for slot in range(self.max_rows):
+            if self.slot_row[slot] is None:
+                self.slot_row[slot] = self._join(slot, *self._draw_request())
         if events:
             events[1].record()
-        t_host = time.perf_counter()
-        R = len(self.rows)
-        for r in self.rows:  # the new token sits at position r.length
-            r.nblk = self.pool.grow(r.table, r.nblk, r.length + 1)
-        tables = np.stack([r.table for r in self.rows])
-        lens = np.array([r.length + 1 for r in self.rows], dtype=np.int32)
+        rows = self.rows
+        R = len(rows)
         k, v, q = self.step_draws(self.step_no, R)
-        tab_d = torch.from_numpy(tables).to(self.dev)
-        pos_d = torch.from_numpy(lens - 1).to(self.dev)
-        rot_d = torch.arange(R, dtype=torch.int32, device=self.dev)
-        lens_d = torch.from_numpy(lens).to(self.dev)
         out = torch.empty((R, self.H, 128), dtype=torch.float16, device=self.dev)
-        if self.shared_decode:
-            marks = torch.from_numpy(np.array([1 if r.shared else 0 for r in self.rows], dtype=np.int32)).to(self.dev)
+
+        t_host = time.perf_counter()
+        slots = np.array([r.slot for r in rows], dtype=np.int64)
+        lens = np.array([r.length + 1 for r in rows], dtype=np.int32)
+        need = np.zeros(self.max_rows, dtype=np.int32)
+        need[slots] = lens  # the new token sits at position r.length
+        grown = self.pool.grow_rows(self.tables, self.tlen, need)
+        if grown < self.max_rows:
+            raise RuntimeError("block pool exhausted: the trace's pool is sized so that every row always fits")
+        st = self.step_no % self.STAGES
+        if self._stage_done[st] is not None:
+            self._stage_done[st].synchronize()  # its previous upload has landed
+        buf = self._stage[st]
+        a = buf.numpy()
+        n_tab = R * self.stride
+        a[:n_tab] = self.tables[slots].reshape(-1)
+        a[n_tab:n_tab + R] = lens
+        a[n_tab + R:n_tab + 2 * R] = lens - 1
+        a[n_tab + 2 * R:n_tab + 3 * R] = [1 if r.shared else 0 for r in rows]
+        tab_d, lens_d, pos_d = self.tab_d[:R], self.lens_d[:R], self.pos_d[:R]
+        marks_d, rot_d = self.marks_d[:R], self.rot_d[:R]
+        tab_d.copy_(buf[:n_tab].view(R, self.stride), non_blocking=True)
+        lens_d.copy_(buf[n_tab:n_tab + R], non_blocking=True)
+        pos_d.copy_(buf[n_tab + R:n_tab + 2 * R], non_blocking=True)
+        marks_d.copy_(buf[n_tab + 2 * R:n_tab + 3 * R], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._stage_done[st] = ev
         host_ms = (time.perf_counter() - t_host) * 1e3
         if events:
             events[2].record()
         if self.shared_decode:
             append(self.cache, 0, k, v, pos_d, rot_d, tab_d)
-            decode_attention_prefix(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, marks,
+            decode_attention_prefix(self.cache, 0, out, q, tab_d, lens_d, self.max_ctx, self.scale, marks_d,
                                     self.prefix_tokens // BLOCK_SIZE, self.ws)
         else:
             # each row's new token is appended by the decode launch itself
             decode_attention_append(self.cache, 0, out, q, k, v, tab_d, lens_d, self.max_ctx, self.scale, self.ws)
         if events:
             events[3].record()
-        snap = {"step": self.step_no, "reqs": [r.req for r in self.rows], "lens": lens.copy(),
-                "gen_index": [r.generated for r in self.rows], "tables": tables.copy(), "out": out,
-                "host_ms": host_ms}
+        tables = self.tables[slots].copy()
+        snap = {"step": self.step_no, "reqs": [r.req for r in rows], "lens": lens.copy(),
+                "gen_index": [r.generated for r in rows], "tables": tables, "out": out, "host_ms": host_ms}
         self.log["steps"].append({"step": self.step_no, "reqs": snap["reqs"], "lens": lens.copy(),
                                   "new_pos": (lens - 1).copy()})
-        for r in self.rows:
+        for r in rows:
             r.generated += 1
         self.step_no += 1
         return snap
@@ -200,5 +251,4 @@ class ContinuousBatchTrace:
     def drain(self):
         for r in self.rows:
             self._leave(r)
-        self.rows = []
         self.pool.free(self.prefix_ids)

@@ -2,9 +2,12 @@
 
 The 7,152-block, 32-layer pool (60 GB) is filled on the device with seeded
 N(0,1) values; the blocks the sampled layers use are read back before any
-kernel runs.  The library appends the step's tokens on every layer and runs
-decode attention; the oracle appends the same tokens itself and recomputes
-every row of the sampled layers."""
+kernel runs.  On every layer the library appends the step's tokens and runs
+decode attention (pkv_append, then pkv_decode_attention); then the same step
+runs again as the benchmark runs it, one pkv_decode_attention_append call per
+layer.  The second pass rewrites the same token bits, so both passes must
+give the same output bits; the oracle appends the same tokens itself and
+recomputes every row of the sampled layers."""
 import numpy as np
 import pytest
 
@@ -48,8 +51,14 @@ def _run(batch, layers, seed):
     for l in range(NL):
         pkv.append(cache, l, t(batch.k_new[l]), t(batch.v_new[l]), pos, rot, tables)
         pkv.decode_attention(cache, l, out[l], t(batch.q[l]), tables, lens, maxL, SCALE, ws)
+    fused = torch.empty_like(out)
+    for l in range(NL):
+        pkv.decode_attention_append(cache, l, fused[l], t(batch.q[l]), t(batch.k_new[l]), t(batch.v_new[l]), tables,
+                                    lens, maxL, SCALE, ws)
     torch.cuda.synchronize()
-    got = out.cpu().numpy().astype(np.float64)
+    assert torch.equal(fused.view(torch.int16), out.view(torch.int16)), "appending decode differs from append + decode"
+    say(f"  {batch.name}: the appending decode gives the same bits as append + decode on all {NL} layers")
+    got = fused.cpu().numpy().astype(np.float64)
     for l in layers:
         slab = before[l].copy()
         index = {int(b): i for i, b in enumerate(ids)}

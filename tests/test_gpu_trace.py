@@ -1,21 +1,16 @@
-"""Continuous-batching trace on the GPU: rows join and leave every step, long
-prompts share ref-counted prefix blocks, tables grow through the library's
-block pool.  Decode outputs of sampled steps are checked against the fp64
-oracle, which rebuilds every row's context from the seeded draws (and the
-prefix blocks' initial contents) without reading anything the kernels wrote;
-pool invariants are checked every step and after the drain."""
-import numpy as np
+"""Continuous-batching trace on the GPU at a small size: rows join and leave
+every step, long prompts share ref-counted prefix blocks, tables grow through
+the library's block pool.  Decode outputs of sampled steps are checked against
+the fp64 oracle, which rebuilds every row's context from the seeded draws (and
+the prefix blocks' initial contents) without reading anything the kernels
+wrote; pool invariants are checked every step and after the drain.  The full
+size runs in test_gpu_trace_full.py."""
 import pytest
 
-import oracle.paged as opaged
 from tests.gpu_util import say, torch_cuda
-from tests.tolerance import assert_close
+from tests.trace_check import TraceChecker
 
 pytestmark = pytest.mark.gpu
-
-
-def _host_bits(t):
-    return t.contiguous().cpu().view(__import__("torch").int16).numpy().view(np.uint16)
 
 
 @pytest.mark.parametrize("shared_decode", [False, True], ids=["plain-decode", "shared-prefix-decode"])
@@ -26,53 +21,25 @@ def test_trace_parity_and_pool_invariants(shared_decode):
     NB = 3000
     tr = ContinuousBatchTrace(torch, seed=11, num_blocks=NB, max_rows=8, prefix_tokens=512, prompt_range=(50, 1400),
                               answer_range=(1, 40), heads=32, shared_decode=shared_decode)
-    prefix = tr.prefix_ids.copy()
-    npre = len(prefix)
-    # the prefix blocks' contents as drawn, read back before any kernel runs
-    pre_slab = _host_bits(tr.pool_d[torch.from_numpy(prefix.astype(np.int64)).to(tr.dev), 0])
-    pre_map = {int(b): pre_slab[i] for i, b in enumerate(prefix)}
-    # where every decode token came from: (req, pos) -> (step, index in that step)
-    origin = {}
-    steps = 60
-    checked = 0
-    for s in range(steps):
+    chk = TraceChecker(tr)
+    npre = len(tr.prefix_ids)
+    for s in range(60):
         snap = tr.step()
-        st = tr.log["steps"][-1]
-        for j, (req, pos) in enumerate(zip(st["reqs"], st["new_pos"])):
-            origin[(req, int(pos))] = (s, j)
+        chk.record(snap)
         # pool invariants: prefix held once by the trace plus once per sharing row
         sharers = sum(1 for r in tr.rows if r.shared)
-        for b in prefix:
+        for b in tr.prefix_ids:
             assert tr.pool.ref_count(int(b)) == 1 + sharers
         held = sum(r.nblk - r.shared // 16 for r in tr.rows)
         assert tr.pool.num_free + held + npre == NB
         if s % 7 == 3:
             say(f"trace step {s} (shared_decode={shared_decode}): rows {len(snap['reqs'])} lens {list(snap['lens'])}")
-            got = snap["out"].float().cpu().numpy()
-            joins = {j[0]: j for j in tr.log["joins"]}
-            for j, req in enumerate(snap["reqs"]):
-                _, prompt, _, shared, _ = joins[req]
-                L = int(snap["lens"][j])
-                K = np.empty((32, L, 128))
-                V = np.empty((32, L, 128))
-                if shared:
-                    pk, pv = opaged.gather_kv(pre_map, prefix, shared)
-                    K[:, :shared], V[:, :shared] = pk, pv
-                if prompt > shared:
-                    k, v = tr.prompt_kv(req, shared, prompt)
-                    K[:, shared:prompt] = k.float().cpu().numpy().transpose(1, 0, 2)
-                    V[:, shared:prompt] = v.float().cpu().numpy().transpose(1, 0, 2)
-                for pos in range(prompt, L):
-                    s2, j2 = origin[(req, pos)]
-                    k, v, _ = tr.step_draws(s2, len(tr.log["steps"][s2]["reqs"]))
-                    K[:, pos] = k[j2].float().cpu().numpy()
-                    V[:, pos] = v[j2].float().cpu().numpy()
-                _, _, q = tr.step_draws(s, len(snap["reqs"]))
-                ref = opaged.attention(q[j:j + 1].float().cpu().numpy().astype(np.float64), K, V, [L - 1], tr.scale)
-                assert_close(got[j], ref[0], f"step {s} row {j}")
-                checked += 1
-    assert checked >= 40
+            chk.keep(snap)
     assert tr.next_req > 8  # rows left and were refilled
     tr.drain()
     assert tr.pool.num_free == NB
     assert all(tr.pool.ref_count(b) == 0 for b in range(NB))
+    tot = chk.check()
+    say(f"trace parity: {tot}")
+    assert tot["rows"] >= 40
+    assert tot["bad"] == 0 and tot["nan"] == 0, tot

@@ -1,0 +1,61 @@
+"""The continuous-batching trace at its full size, checked against the oracle.
+
+64 rows over a 36,864-block one-layer pool (32 heads x 128, FP16), prompts
+U{50..8000}, answers U{1..1000}, a 2,000-token prefix held in 125 ref-counted
+blocks and shared by every prompt that long, 300 steps with rows leaving and
+joining every step (LLM inference batching, faangrind: problem statement and
+test plan "Correctness"; Serving LLMs, "Prefix caching").  Every row of an
+early, a middle and the last step is compared with the fp64 oracle, which
+rebuilds the row's context from the seeded draws and the prefix blocks' initial
+contents.  Both decode paths run: the appending decode, and the shared-prefix
+decode whose prefix tiles hold up to 32 sharing rows (two tiles per head and
+range at 64 rows).  Pool reference counts are checked every step and the pool
+drains back to a full free list."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import say, torch_cuda
+from tests.trace_check import TraceChecker
+
+pytestmark = pytest.mark.gpu
+
+NB = 36864
+STEPS = 300
+SAMPLED = (5, 150, STEPS - 1)
+
+
+@pytest.mark.parametrize("shared_decode", [False, True], ids=["appending-decode", "shared-prefix-decode"])
+def test_trace_full_size_parity(shared_decode):
+    torch = torch_cuda()
+    from paged_kv_cache_pkv_amd.trace import ContinuousBatchTrace
+
+    tr = ContinuousBatchTrace(torch, seed=3, num_blocks=NB, max_rows=64, prefix_tokens=2000,
+                              prompt_range=(50, 8000), answer_range=(1, 1000), shared_decode=shared_decode)
+    chk = TraceChecker(tr)
+    npre = len(tr.prefix_ids)
+    assert npre == 125
+    max_sharers = 0
+    for s in range(STEPS):
+        snap = tr.step()
+        chk.record(snap)
+        sharers = sum(1 for r in tr.rows if r.shared)
+        max_sharers = max(max_sharers, sharers)
+        for b in tr.prefix_ids[:: 31]:
+            assert tr.pool.ref_count(int(b)) == 1 + sharers
+        held = sum(r.nblk - r.shared // 16 for r in tr.rows)
+        assert tr.pool.num_free + held + npre == NB
+        if s in SAMPLED:
+            chk.keep(snap)
+            say(f"trace step {s} ({'shared-prefix' if shared_decode else 'appending'} decode): {len(snap['reqs'])} "
+                f"rows, {sharers} sharing the prefix, context {int(snap['lens'].min())}..{int(snap['lens'].max())}")
+    assert max_sharers > 32, "the prefix must be shared by more rows than one tile holds"
+    joins = len(tr.log["joins"])
+    assert joins > 64 + 20, "rows must leave and be refilled"
+    tr.drain()
+    assert tr.pool.num_free == NB
+    assert all(tr.pool.ref_count(int(b)) == 0 for b in tr.prefix_ids)
+    tot = chk.check(log=say)
+    say(f"trace parity: {tot}")
+    assert tot["rows"] == sum(len(smp[1]) for smp in chk.samples) >= 3 * 64
+    assert tot["bad"] == 0 and tot["nan"] == 0, tot
+    assert tot["max_abs"] <= 2e-3 and tot["max_rel"] <= 1e-2, tot

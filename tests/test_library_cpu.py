@@ -363,3 +363,40 @@ def test_validation_chunked_prefill_args():
     assert call(wsb=need - 1) == -6
     assert call(ws=ctypes.c_void_p(0x200010), wsb=need) == -6  # 256-byte alignment
     assert b"workspace" in L.pkv_last_error()
+
+
+def test_pool_grow_rows_matches_model():
+    """pkv_grow_rows grows each row as the oracle pool model's grow does, rows
+    in order, each all or nothing, stopping at the first row the free list
+    cannot cover; bad arguments of any row change nothing."""
+    rng = np.random.default_rng(23)
+    N, R, stride = 120, 6, 12
+    perm = rng.permutation(N).astype(np.int32)
+    lib_pool = pkv.BlockPool(N, perm)
+    model = opool.BlockPool(N, perm)
+    tables = np.zeros((R, stride), dtype=np.int32)
+    lens = np.zeros(R, dtype=np.int32)
+    mtables = [[] for _ in range(R)]
+    tokens = np.zeros(R, dtype=np.int64)
+    for step in range(40):
+        tokens += rng.integers(0, 40, R)
+        tokens = np.minimum(tokens, 16 * stride)
+        got = lib_pool.grow_rows(tables, lens, tokens)
+        want = R
+        for r in range(R):
+            if not model.grow(mtables[r], int(tokens[r])):
+                want = r
+                break
+        assert got == want
+        for r in range(R):
+            assert list(tables[r, :lens[r]]) == mtables[r]
+        assert list(lib_pool.free_list()) == model.free
+        if got < R:  # preempt the row that came up short: release it and start it over
+            lib_pool.free(tables[got, :lens[got]])
+            model.release(mtables[got])
+            lens[got], mtables[got], tokens[got] = 0, [], 0
+    before = (tables.copy(), lens.copy(), lib_pool.num_free)
+    with pytest.raises(pkv.PkvError) as e:
+        lib_pool.grow_rows(tables, lens, np.full(R, 16 * stride + 1))
+    assert e.value.name == "INVALID_ARG"
+    assert np.array_equal(tables, before[0]) and np.array_equal(lens, before[1]) and lib_pool.num_free == before[2]
