@@ -206,79 +206,122 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
     }
 
 
-def _run_trace(torch, steps, warm, shared_decode):
+TRACE_SAMPLED = (10, 150, 299)  # timed-step indices whose outputs the oracle leg checks
+TRACE_CHECK_ROWS = range(0, 64, 4)  # 16 of the 64 rows of each sampled step
+
+
+def _run_trace(torch, steps, warm, shared_decode, cold_steps=20, checker=False):
     from paged_kv_cache_pkv_amd.trace import ContinuousBatchTrace
 
     tr = ContinuousBatchTrace(torch, seed=3, num_blocks=36864, max_rows=64, prefix_tokens=2000,
                               prompt_range=(50, 8000), answer_range=(1, 1000), shared_decode=shared_decode)
+    chk = None
+    if checker:
+        from tests.trace_check import TraceChecker  # test infrastructure for the oracle leg
+
+        chk = TraceChecker(tr)
     for _ in range(warm):
-        tr.step()
+        snap = tr.step()
+        if chk:
+            chk.record(snap)
     torch.cuda.synchronize()
     rec = []
-    for _ in range(steps):
+    for i in range(steps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         snap = tr.step(events=ev)
+        if chk:
+            chk.record(snap)
+            if i in TRACE_SAMPLED:
+                chk.keep(snap)
         sharers = sum(1 for r in tr.rows if r.shared)
         rec.append((ev, int(snap["lens"].sum()), sharers, snap["host_ms"]))
     torch.cuda.synchronize()
+    # cold: the 256 MB last-level cache scrubbed (a 512 MB write, not timed)
+    # before each step's decode part
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=tr.dev)
+    cold = []
+    for _ in range(cold_steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        snap = tr.step(events=ev, before_decode=lambda: scrub.fill_(1))
+        if chk:
+            chk.record(snap)
+        cold.append(ev)
+    torch.cuda.synchronize()
+    del scrub
+    cold_ms = np.array([e[2].elapsed_time(e[3]) for e in cold])
     fill_ms = np.array([e[0].elapsed_time(e[1]) for e, _, _, _ in rec])
     step_ms = np.array([e[2].elapsed_time(e[3]) for e, _, _, _ in rec])
     with_host_ms = np.array([e[1].elapsed_time(e[3]) for e, _, _, _ in rec])
     host_ms = np.array([h for _, _, _, h in rec])
     tokens = np.array([t for _, t, _, _ in rec], dtype=np.float64)
     sharers = np.array([n for _, _, n, _ in rec], dtype=np.float64)
-    joins = sum(1 for j in tr.log["joins"] if j[4] >= warm)
+    joins = sum(1 for j in tr.log["joins"] if warm <= j[4] < warm + steps)
     prefix = tr.prefix_tokens
     tr.drain()
     assert tr.pool.num_free == 36864, "trace leaked blocks"
-    return step_ms, fill_ms, tokens, sharers, joins, prefix, with_host_ms, host_ms
+    del tr.pool_d
+    return dict(step_ms=step_ms, fill_ms=fill_ms, tokens=tokens, sharers=sharers, joins=joins, prefix=prefix,
+                with_host_ms=with_host_ms, host_ms=host_ms, cold_ms=cold_ms, checker=chk)
 
 
-def measure_trace(torch, steps=300, warm=5):
+def measure_trace(torch, steps=300, warm=5, checkers=None):
     """Continuous-batching trace: up to 64 rows over a 36,864-block one-layer
     pool, prompts U{50..8000}, answers U{1..1000}, a 2,000-token prefix
     shared by reference counts; rows leave and are refilled every step.
     The decode part of a step (append one token per row, decode) is timed
     with events around its launches, separately from the fill of joining
-    rows; the host work before the launches (table growth, the step's
-    synthetic inputs and their pageable upload) is timed on the host and
-    reported beside it, as is the step with it.  The same seeded trace runs
-    twice: with plain decode, and with the shared-prefix decode that reads
-    the prefix once per step for every 32 rows holding it."""
-    step_ms, fill_ms, tokens, sharers, joins, prefix, wh_ms, host_ms = _run_trace(torch, steps, warm, False)
-    s_ms, _, s_tokens, s_sharers, _, _, s_wh_ms, s_host_ms = _run_trace(torch, steps, warm, True)
-    assert np.array_equal(tokens, s_tokens) and np.array_equal(sharers, s_sharers), "the two traces diverged"
+    rows; the host's preparation before the launches (one batched table
+    growth, the pinned upload of tables and lengths) is timed on the host and
+    reported beside it, as is the step with it.  After the timed steps, 20
+    more steps run with the last-level cache scrubbed before each decode part
+    (cold).  The same seeded trace runs twice: with plain decode, and with the
+    shared-prefix decode that reads the prefix once per step for every 32 rows
+    holding it.  With `checkers` (a list), the outputs of three sampled steps
+    are kept for the oracle leg."""
+    want = checkers is not None
+    p = _run_trace(torch, steps, warm, False, checker=want)
+    s = _run_trace(torch, steps, warm, True, checker=want)
+    if want:
+        checkers.extend([("appending", p["checker"]), ("shared_prefix", s["checker"])])
+    tokens, sharers, prefix = p["tokens"], p["sharers"], p["prefix"]
+    assert np.array_equal(tokens, s["tokens"]) and np.array_equal(sharers, s["sharers"]), "the two traces diverged"
     # tokens the shared-prefix decode reads: the prefix once per tile of up to 32 sharing rows
     physical = tokens - prefix * (sharers - np.ceil(sharers / 32.0))
-    return {
+
+    def leg(d, extra):
+        ms = d["step_ms"]
+        out = {
+            "decode_step_ms_p50": float(np.percentile(ms, 50)),
+            "decode_step_ms_p90": float(np.percentile(ms, 90)),
+            "decode_step_ms_max": float(ms.max()),
+            "decode_step_cold_ms_p50": float(np.percentile(d["cold_ms"], 50)),
+            "decode_step_with_host_ms_p50": float(np.percentile(d["with_host_ms"], 50)),
+            "host_prep_ms_p50": float(np.percentile(d["host_ms"], 50)),
+            "kv_tokens_per_s": float(tokens.sum() / (ms.sum() / 1e3)),
+            "logical_tb_s": float(tokens.sum() * LAYER_TOKEN_BYTES / (ms.sum() / 1e3) / 1e12),
+        }
+        out.update(extra)
+        return out
+
+    rec = leg(p, {
         "workload": "continuous-batching trace: <=64 rows, one layer 32x128 FP16, 36,864-block pool, "
                     "prompts U{50..8000}, answers U{1..1000}, 2,000-token prefix shared by 125 ref-counted blocks",
         "steps": steps,
-        "decode_step_ms_p50": float(np.percentile(step_ms, 50)),
-        "decode_step_ms_p90": float(np.percentile(step_ms, 90)),
-        "decode_step_ms_max": float(step_ms.max()),
-        "decode_step_with_host_ms_p50": float(np.percentile(wh_ms, 50)),
-        "host_prep_ms_p50": float(np.percentile(host_ms, 50)),
+        "cold_steps": int(len(p["cold_ms"])),
         "logical_kv_tokens_per_step_mean": float(tokens.mean()),
-        "kv_tokens_per_s": float(tokens.sum() / (step_ms.sum() / 1e3)),
-        "logical_tb_s": float(tokens.sum() * LAYER_TOKEN_BYTES / (step_ms.sum() / 1e3) / 1e12),
-        "joins": joins,
-        "fill_ms_total": float(fill_ms.sum()),
+        "joins": p["joins"],
+        "fill_ms_total": float(p["fill_ms"].sum()),
         "pool_drained": True,
-        "shared_prefix_decode": {
-            "decode_step_ms_p50": float(np.percentile(s_ms, 50)),
-            "decode_step_ms_p90": float(np.percentile(s_ms, 90)),
-            "decode_step_ms_max": float(s_ms.max()),
-            "decode_step_with_host_ms_p50": float(np.percentile(s_wh_ms, 50)),
-            "host_prep_ms_p50": float(np.percentile(s_host_ms, 50)),
-            "sharing_rows_per_step_mean": float(sharers.mean()),
-            "read_kv_tokens_per_step_mean": float(physical.mean()),
-            "kv_tokens_per_s": float(tokens.sum() / (s_ms.sum() / 1e3)),
-            "logical_tb_s": float(tokens.sum() * LAYER_TOKEN_BYTES / (s_ms.sum() / 1e3) / 1e12),
-            "read_tb_s": float(physical.sum() * LAYER_TOKEN_BYTES / (s_ms.sum() / 1e3) / 1e12),
-            "speedup_vs_plain": float(step_ms.sum() / s_ms.sum()),
-        },
-    }
+        "host_prep_note": "one pkv_grow_rows call, staging into pinned memory and the async uploads; "
+                          "the synthetic draws are not counted",
+    })
+    rec["shared_prefix_decode"] = leg(s, {
+        "sharing_rows_per_step_mean": float(sharers.mean()),
+        "read_kv_tokens_per_step_mean": float(physical.mean()),
+        "read_tb_s": float(physical.sum() * LAYER_TOKEN_BYTES / (s["step_ms"].sum() / 1e3) / 1e12),
+        "speedup_vs_plain": float(p["step_ms"].sum() / s["step_ms"].sum()),
+    })
+    return rec
 
 
 def parse():
@@ -298,6 +341,51 @@ def parse():
                     help="after the run, copy a buffer of this many MiB three times (a known-size kernel for "
                          "calibrating HBM byte counters)")
     return ap.parse_args()
+
+
+def measure_bandwidth(torch, pkv, cache, tables, tlen, stream):
+    """Achievable read bandwidth on this machine, from the probes in
+    libpkv_probe.so: the (block, layer) slabs one decode step of the average
+    mix reads (the same 256 KiB slabs, every layer in turn, one workgroup per
+    slab), and a plain 2 GiB stream; each with the streaming (non-temporal)
+    cache policy the decode kernels use and with ordinary loads."""
+    from paged_kv_cache_pkv_amd import probe
+
+    pool = cache.pool
+    dev = pool.device
+    NL, H = int(pool.shape[1]), int(pool.shape[3])
+    slab_bytes = 2 * H * 16 * 128 * 2
+    ids = np.concatenate([tables[r, :tlen[r]] for r in range(tables.shape[0])]).astype(np.int64)
+    idx = torch.from_numpy(np.stack([ids * NL + l for l in range(NL)]).astype(np.int32)).to(dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    slab_nt = timed(lambda i: probe.slab_read(pool, idx[i % NL], slab_bytes, sink, True, stream), 2 * NL)
+    slab_pl = timed(lambda i: probe.slab_read(pool, idx[i % NL], slab_bytes, sink, False, stream), 2 * NL)
+    buf = torch.empty((1 << 31) - 4096, dtype=torch.uint8, device=dev)
+    stream_nt = timed(lambda i: probe.stream_read(buf, sink, True, stream), 10)
+    stream_pl = timed(lambda i: probe.stream_read(buf, sink, False, stream), 10)
+    nslab = float(len(ids) * slab_bytes)
+    del buf
+    return {
+        "probe": "libpkv_probe.so (include/pkv_probe.h)",
+        "slab_read_gb_s": nslab / (slab_nt / 1e3) / 1e9,
+        "slab_read_plain_gb_s": nslab / (slab_pl / 1e3) / 1e9,
+        "slab_read_note": f"{len(ids)} (block, layer) slabs of {slab_bytes} B per launch: the K and V one "
+                          "average-mix decode launch reads, non-temporal (plain: ordinary loads)",
+        "stream_read_gb_s": ((1 << 31) - 4096) / (stream_nt / 1e3) / 1e9,
+        "stream_read_plain_gb_s": ((1 << 31) - 4096) / (stream_pl / 1e3) / 1e9,
+    }
 
 
 def measure_block_copies(torch, pkv, cache, free_ids, stream, n=64, reps=10):
@@ -461,10 +549,12 @@ def measure_long_context(torch, pkv, cache, stream, steps=5, warm=2):
     }
 
 
-def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, warm=3):
+def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, warm=3, payload=None):
     """Grouped-query decode: the average mix's tables and lengths over a
     32-layer pool of 8 KV heads (2 MiB blocks), 32 query heads (groups of 4);
-    per layer one decode launch.  Bytes = K and V of 8 heads per token."""
+    per layer one decode launch.  Bytes = K and V of 8 heads per token.  With
+    `payload` (a list), layer 0's first output and the blocks it read are
+    kept for the oracle leg."""
     from workloads import SCALE, fill_normal_fp16_device
 
     NB, NL = 7152, 32
@@ -480,6 +570,14 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
     q = torch.from_numpy(rng.standard_normal((NL, R, q_heads, 128), dtype=np.float32).astype(np.float16)).to(dev)
     out = torch.empty((R, q_heads, 128), dtype=torch.float16, device=dev)
     ws = torch.empty(pkv.decode_workspace_size_gqa(cache, q_heads, R, maxL), dtype=torch.uint8, device=dev)
+    if payload is not None:
+        nblk = [-(-int(L) // 16) for L in batch.context_lens]
+        ids = np.unique(np.concatenate([batch.block_tables[r, :nblk[r]] for r in range(R)]))
+        slab = pool[torch.from_numpy(ids.astype(np.int64)).to(dev), 0].cpu().numpy().view(np.uint16)
+        pkv.decode_attention_gqa(cache, q_heads, 0, out, q[0], tables, lens, maxL, SCALE, ws, stream=stream)
+        torch.cuda.synchronize()
+        payload.append((ids, slab, q[0].cpu().numpy().view(np.uint16), out.cpu().numpy().view(np.uint16),
+                        batch.block_tables, batch.context_lens, q_heads // kv_heads))
 
     def step():
         for l in range(NL):
@@ -615,6 +713,135 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
     }
 
 
+# ---------------- oracle leg (CPU baseline and parity), run in spawned worker processes
+# Each worker is a fresh interpreter (spawn: the GPU process is never forked
+# into a worker) with BLAS limited to one thread; the read-back blocks sit in
+# one shared-memory segment that every worker maps.
+_W = {}
+
+
+def _oracle_worker_init(shm_name, shape, ids, tables, lens, q_bits):
+    from multiprocessing import shared_memory
+
+    import threadpoolctl
+
+    threadpoolctl.threadpool_limits(1)
+    shm = shared_memory.SharedMemory(name=shm_name)
+    _W["shm"] = shm
+    _W["slab"] = np.ndarray(shape, dtype=np.uint16, buffer=shm.buf)  # [layers, blocks, 2, H, 16, D]
+    _W["index"] = {int(b): i for i, b in enumerate(ids)}
+    _W["tables"], _W["lens"], _W["q"] = tables, lens, q_bits       # q: [layers, R, H, D]
+
+
+def _oracle_task(li, r):
+    """fp64 oracle decode of row r on sampled layer li: the gather through the
+    block table, then softmax(q K^T / sqrt(128)) V."""
+    import oracle.paged as opaged
+    from workloads import SCALE
+
+    slab, index = _W["slab"][li], _W["index"]
+
+    class Blocks:
+        def __getitem__(self, b):
+            return slab[index[int(b)]]
+
+    out = opaged.decode(Blocks(), _W["q"][li], _W["tables"], _W["lens"], SCALE, rows=[r])[0]
+    return li, r, out
+
+
+def _noop(x):
+    return x
+
+
+def oracle_cpu_baseline(args, sample, tables, lens, q_bits, gpu_outs, layer_names):
+    """Time the fp64 oracle on the machine's host cores over (row, layer) tasks of
+    the benchmark's first step (the sampled layers' blocks were read back
+    before any kernel ran and the oracle appended the step's tokens itself),
+    for about args.cpu_seconds of wall time.  The first pass over every task
+    is also compared with the GPU's outputs of that step."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import resource
+    from multiprocessing import shared_memory
+
+    from tests.tolerance import compare
+
+    ids, slab, t_d2h = sample
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16))
+    shm = shared_memory.SharedMemory(create=True, size=slab.nbytes)
+    try:
+        np.ndarray(slab.shape, dtype=np.uint16, buffer=shm.buf)[...] = slab
+        ctx = mp.get_context("spawn")
+        R = len(lens)
+        tasks = [(li, r) for li in range(slab.shape[0]) for r in range(R)]
+        tok = {(li, r): int(lens[r]) for li, r in tasks}
+        cpu0 = resource.getrusage(resource.RUSAGE_CHILDREN)
+        with cf.ProcessPoolExecutor(workers, mp_context=ctx, initializer=_oracle_worker_init,
+                                    initargs=(shm.name, slab.shape, ids, tables, lens, q_bits)) as ex:
+            list(ex.map(_noop, range(4 * workers)))  # every worker started and initialised
+            t0 = time.perf_counter()
+            pending, done, n_sub, first = set(), 0, 0, {}
+            tokens = 0
+            while True:
+                while len(pending) < 2 * workers and (time.perf_counter() - t0 < args.cpu_seconds
+                                                      or n_sub < len(tasks)):
+                    pending.add(ex.submit(_oracle_task, *tasks[n_sub % len(tasks)]))
+                    n_sub += 1
+                if not pending:
+                    break
+                fin, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+                for f in fin:
+                    li, r, out = f.result()
+                    tokens += tok[(li, r)]
+                    done += 1
+                    first.setdefault((li, r), out)
+            wall = time.perf_counter() - t0
+        cpu1 = resource.getrusage(resource.RUSAGE_CHILDREN)
+    finally:
+        shm.close()
+        shm.unlink()
+    busy = (cpu1.ru_utime + cpu1.ru_stime) - (cpu0.ru_utime + cpu0.ru_stime)
+    parity = {"layers": layer_names, "rows": R, "max_abs": 0.0, "max_rel": 0.0, "bad": 0}
+    for (li, r), ref in first.items():
+        c = compare(gpu_outs[li][r], ref)
+        parity["max_abs"] = max(parity["max_abs"], c["max_abs"])
+        parity["max_rel"] = max(parity["max_rel"], c["max_rel"])
+        parity["bad"] += c["bad"] + c["nan"]
+    parity["pass"] = parity["bad"] == 0
+    nl = 32
+    baseline = {
+        "value": (tokens / nl) / wall, "unit": "KV-tokens/s", "cores": workers, "kind": "oracle",
+        "sample": f"fp64 NumPy oracle decode of (row, layer) tasks of the average-mix step (rows 0..{R - 1}, "
+                  f"layers {layer_names}), {done} tasks = {tokens} one-layer KV-tokens in {wall:.1f} s on "
+                  f"{workers} worker processes, BLAS at 1 thread each; value = one-layer tokens / 32 / s",
+        "cpu_seconds": busy, "wall_seconds": wall, "cpu_time_over_wall": busy / wall,
+        "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+        "d2h_readback_s": t_d2h,
+        "d2h_note": "the sampled layers' blocks copied to host memory before any kernel ran; not in the timed run",
+    }
+    return baseline, parity
+
+
+def gqa_parity(payload):
+    """The grouped-query leg's first decode (layer 0, G = 4, weights rounded to
+    FP16 before P.V) against the fp64 oracle."""
+    import oracle.paged as opaged
+    from tests.tolerance import compare
+    from workloads import SCALE
+
+    ids, slab, q0, out0, tables, lens, group = payload
+    index = {int(b): i for i, b in enumerate(ids)}
+
+    class Blocks:
+        def __getitem__(self, b):
+            return slab[index[int(b)]]
+
+    ref = opaged.decode(Blocks(), q0, tables, lens, SCALE, group=group)
+    c = compare(out0.view(np.float16).astype(np.float64), ref)
+    return {"layer": 0, "rows": int(len(lens)), "group": group, "max_abs": c["max_abs"], "max_rel": c["max_rel"],
+            "bad": c["bad"] + c["nan"], "pass": c["bad"] + c["nan"] == 0}
+
+
 def log(args, msg):
     if not args.quiet:
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -658,9 +885,8 @@ def main():
     # host block pool: shuffled free list, rows allocated in order
     bp = pkv.BlockPool(NB, batch.free_list)
     tables = np.zeros((R, stride), dtype=np.int32)
-    tlen = np.zeros(R, dtype=np.int64)
-    for r in range(R):
-        tlen[r] = bp.grow(tables[r], 0, int(lens0[r]))
+    tlen = np.zeros(R, dtype=np.int32)
+    tlen[:] = [bp.grow(tables[r], 0, int(lens0[r])) for r in range(R)]
     for r in range(R):  # the C++ pool hands out the ids the generator's LIFO reading predicts
         assert np.array_equal(tables[r, :tlen[r]], batch.block_tables[r, :tlen[r]])
 
@@ -678,13 +904,15 @@ def main():
     # pinned staging, one set per step so the host never overwrites a buffer in flight
     stage = [torch.empty(R * stride + 2 * R, dtype=torch.int32, pin_memory=True) for _ in range(total_steps)]
 
-    # ---------------- CPU baseline input: blocks read back before any kernel touches the pool
+    # ---------------- oracle-leg input: two layers' blocks read back before any kernel touches the pool
+    ORACLE_LAYERS = (0, NL - 1)
     cpu_sample = None
     if not args.no_cpu_baseline:
         ids = np.unique(np.concatenate([tables[r, :tlen[r]] for r in range(R)]))
         torch.cuda.synchronize()
         t_d2h = time.perf_counter()
-        slab = pool_d[torch.from_numpy(ids.astype(np.int64)).to(dev), 0].cpu().numpy().view(np.uint16)
+        ids_d = torch.from_numpy(ids.astype(np.int64)).to(dev)
+        slab = np.stack([pool_d[ids_d, l].cpu().numpy().view(np.uint16) for l in ORACLE_LAYERS])
         t_d2h = time.perf_counter() - t_d2h
         cpu_sample = (ids, slab, t_d2h)
 
@@ -692,11 +920,10 @@ def main():
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
     def host_step(k):
-        """Grow tables for this step's new token, stage the upload."""
+        """Grow tables for this step's new token (one pkv_grow_rows call), stage the upload."""
         lens = lens0 + k
-        for r in range(R):
-            if tlen[r] * 16 < lens[r]:
-                tlen[r] = bp.grow(tables[r], int(tlen[r]), int(lens[r]))
+        if bp.grow_rows(tables, tlen, lens) != R:
+            raise SystemExit("block pool exhausted")
         buf = stage[k]
         a = buf.numpy()
         a[: R * stride] = tables.reshape(-1)
@@ -707,58 +934,43 @@ def main():
         pos_d.copy_(buf[R * stride + R:], non_blocking=True)
         return int(lens.sum())
 
-    # Per-launch timing: two decode launches per timed step carry HIP events
-    # (layers rotate so every layer is sampled); bracketing all 32 would add
-    # about 5% to the step.
-    samples = []  # (step index, layer, start event, end event)
-    spare_events = events(4 * args.steps)
-
-    def sampled_layers(i):
-        return {(2 * i) % NL, (2 * i + NL // 2) % NL}
-
-    def gpu_step(i, fused=True):
+    def gpu_step(fused=True):
         """Per layer: the step's append and decode attention.  By default one
         fused call (the range holding each row's new token appends it);
         fused=False runs pkv_append then pkv_decode_attention."""
-        pick = sampled_layers(i) if i is not None else ()
         for l in range(NL):
-            if not fused:
-                pkv.append(cache, l, k_d[l], v_d[l], pos_d, rot_d, tables_d, stream=stream)
-            if l in pick:
-                e0, e1 = spare_events.pop(), spare_events.pop()
-                e0.record(stream)
             if fused:
                 pkv.decode_attention_append(cache, l, out_d[l], q_d[l], k_d[l], v_d[l], tables_d, lens_d, max_ctx,
                                             SCALE, ws_d, stream=stream)
             else:
+                pkv.append(cache, l, k_d[l], v_d[l], pos_d, rot_d, tables_d, stream=stream)
                 pkv.decode_attention(cache, l, out_d[l], q_d[l], tables_d, lens_d, max_ctx, SCALE, ws_d,
                                      stream=stream)
-            if l in pick:
-                e1.record(stream)
-                samples.append((i, l, e0, e1))
 
     log(args, f"rows={R} sum_context={int(lens0.sum())} max_context={int(lens0.max())} ws={ws_bytes}")
-    parity = None
-    step0_out = None
+    step0_outs = None
     for k in range(args.warmup):
         host_step(k)
-        gpu_step(None)
+        gpu_step()
         if k == 0:
             torch.cuda.synchronize()
-            step0_out = out_d[0].cpu().numpy().astype(np.float64)
+            step0_outs = [out_d[l].cpu().numpy().view(np.uint16).view(np.float16).astype(np.float64)
+                          for l in ORACLE_LAYERS]
     torch.cuda.synchronize()
 
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     tokens = 0
+    step_tokens = []
     t_start.record(stream)
     wall0 = time.perf_counter()
     step_ev = events(args.steps + 1)
     for i, k in enumerate(range(args.warmup, args.warmup + args.steps)):
-        step_tokens = host_step(k)
-        tokens += step_tokens
-        step_ev[i].record(stream)
-        gpu_step(i)
+        st = host_step(k)
+        tokens += st
+        step_tokens.append(st)
+        step_ev[i].record(stream)  # after the step's uploads are queued: brackets the 32 layer calls
+        gpu_step()
     step_ev[args.steps].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -772,92 +984,71 @@ def main():
     u0.record(stream)
     for k in range(args.warmup + args.steps, total_steps):
         unfused_tokens += host_step(k)
-        gpu_step(None, fused=False)
+        gpu_step(fused=False)
     u1.record(stream)
     torch.cuda.synchronize()
     unfused_ms = u0.elapsed_time(u1) / UNFUSED_STEPS
 
-    dec_ms = [e0.elapsed_time(e1) for (_, _, e0, e1) in samples]
-    dec_avg_ms = float(np.mean(dec_ms))
-    bytes_per_decode = float(np.mean([int((lens0 + args.warmup + i).sum()) * LAYER_TOKEN_BYTES
-                                      for (i, _, _, _) in samples]))
-    achieved = bytes_per_decode / (dec_avg_ms / 1e3) / 1e9
-    traffic = counted_traffic()
-
     ms_per_step = elapsed_ms / args.steps
     step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
     value = tokens / (elapsed_ms / 1e3)
+    # The dominant kernel is the decode call (split + merge launches, the
+    # append fused).  Its average duration: the events bracketing each step's
+    # 32 back-to-back calls (and nothing else) over the timed steps, / 32.
+    launches = NL * args.steps
+    dec_avg_ms = float(np.sum(step_ms)) / launches
+    bytes_per_decode = float(np.mean(step_tokens)) * LAYER_TOKEN_BYTES
+    achieved = bytes_per_decode / (dec_avg_ms / 1e3) / 1e9
+    traffic = counted_traffic()
 
-    # ---------------- CPU baseline leg: the oracle as it stands, timed on a bounded sample
-    # (layer 0 of step 0, rows in turn).  The oracle appends the step-0 tokens
-    # itself; its outputs are also compared with the GPU's step-0 outputs.
-    parity = None
-    cpu_baseline = None
-    if cpu_sample is not None:
-        import threadpoolctl
-
-        import oracle.paged as opaged
-
-        ids, slab, t_d2h = cpu_sample
-        index = {int(bk): i for i, bk in enumerate(ids)}
-
-        class Blocks:
-            def __getitem__(self, bk):
-                return slab[index[int(bk)]]
-
-        tbl0 = batch.block_tables
-        pos0 = (lens0 - 1).astype(np.int64)
-        for r in range(R):
-            bk, s = opaged.locate(tbl0[r], int(pos0[r]))
-            slab[index[bk], 0, :, s, :] = batch.k_new[0, r]
-            slab[index[bk], 1, :, s, :] = batch.v_new[0, r]
-        t0 = time.perf_counter()
-        c0 = time.process_time()
-        rows_done = tok_done = bad = 0
-        max_abs = 0.0
-        while time.perf_counter() - t0 < args.cpu_seconds and rows_done < 64 * R:
-            r = rows_done % R
-            ref = opaged.decode(Blocks(), batch.q[0], tbl0, lens0, SCALE, rows=[r])[0]
-            rows_done += 1
-            tok_done += int(lens0[r])
-            if rows_done <= R:
-                err = np.abs(step0_out[r] - ref)
-                max_abs = max(max_abs, float(err.max()))
-                bad += int((err > np.maximum(2e-3, 1e-2 * np.abs(ref))).sum())
-        cpu_s = time.perf_counter() - t0
-        busy_s = time.process_time() - c0
-        parity = {"layer": 0, "rows": min(rows_done, R), "max_abs": max_abs, "bad": bad, "pass": bad == 0}
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-        cpu_baseline = {"value": (tok_done / NL) / cpu_s, "unit": "KV-tokens/s",
-                        "cores": max(1, int(round(busy_s / cpu_s))),
-                        "kind": "oracle",
-                        "sample": f"fp64 oracle decode of {rows_done} (row, layer-0) tasks of the same step, "
-                                  f"{tok_done} one-layer tokens in {cpu_s:.1f} s; value = layer-tokens / 32 / s",
-                        "cores_note": "process CPU time / wall time over the timed oracle run",
-                        "cpu_seconds": busy_s, "wall_seconds": cpu_s, "blas_threads": int(threads),
-                        "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
-                        "d2h_readback_s": t_d2h,
-                        "d2h_note": "the sample's blocks (layer 0) copied to host memory before the run, not timed in it"}
-
-    blocks = None
-    long_ctx = None
-    gqa = None
-    fp8 = None
-    tiny = None
+    blocks = long_ctx = gqa = fp8 = tiny = probe = None
+    gqa_payload = [] if cpu_sample is not None else None
     if not args.no_extra:
+        probe = measure_bandwidth(torch, pkv, cache, tables, tlen, stream)
         blocks = measure_block_copies(torch, pkv, cache, bp.free_list(), stream)
         long_ctx = measure_long_context(torch, pkv, cache, stream)
-        gqa = measure_gqa(torch, pkv, batch, stream)
+        del pool_d, cache
+        torch.cuda.empty_cache()
+        gqa = measure_gqa(torch, pkv, batch, stream, payload=gqa_payload)
         fp8 = measure_fp8(torch, pkv, batch, stream)
         tiny = measure_tiny(torch, pkv, dev, stream)
+    else:
+        del pool_d, cache
+        torch.cuda.empty_cache()
 
     prefill = None
     if not args.no_prefill:
         prefill = measure_prefill(torch, pkv, dev, stream)
 
     trace = None
+    checkers = [] if cpu_sample is not None else None
     if not args.no_trace:
-        trace = measure_trace(torch, steps=args.trace_steps)
+        trace = measure_trace(torch, steps=args.trace_steps, checkers=checkers)
+
+    # ---------------- oracle leg: CPU baseline and parity against the fp64 oracle
+    cpu_baseline = parity = None
+    if cpu_sample is not None:
+        log(args, "oracle leg: CPU baseline and parity")
+        pos0 = (lens0 - 1).astype(np.int64)
+        ids, slab, _ = cpu_sample
+        index = {int(bk): i for i, bk in enumerate(ids)}
+        for li, l in enumerate(ORACLE_LAYERS):  # the oracle's own append of step 0's tokens
+            for r in range(R):
+                bk = int(batch.block_tables[r, pos0[r] // 16])
+                slab[li, index[bk], 0, :, pos0[r] % 16, :] = batch.k_new[l, r]
+                slab[li, index[bk], 1, :, pos0[r] % 16, :] = batch.v_new[l, r]
+        q_bits = np.stack([batch.q[l] for l in ORACLE_LAYERS])
+        cpu_baseline, parity = oracle_cpu_baseline(args, cpu_sample, batch.block_tables, lens0.astype(np.int32),
+                                                   q_bits, step0_outs, list(ORACLE_LAYERS))
+        if gqa is not None and gqa_payload:
+            gqa["parity"] = gqa_parity(gqa_payload[0])
+        if trace is not None and checkers:
+            for name, chk in checkers:
+                tot = chk.check(rows=TRACE_CHECK_ROWS)
+                tot["rows_per_step"] = len(TRACE_CHECK_ROWS)
+                tot["timed_steps_sampled"] = list(TRACE_SAMPLED)
+                tot["pass"] = tot["bad"] == 0 and tot["nan"] == 0
+                (trace if name == "appending" else trace["shared_prefix_decode"])["parity"] = tot
 
     rec = {
         "metric": METRIC,
@@ -875,7 +1066,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 storage, f32 accumulation",
         "data": "synthetic",
         "config": {
             "workload": "average-mix decode step: 32 rows x 32 layers, 32 heads x 128, FP16 KV in 7152 blocks of 16",
@@ -888,9 +1079,11 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "pkv_decode_attention_append (split + merge launches, the append fused), one layer",
                      "avg_launch_ms": dec_avg_ms, "bytes_per_launch": bytes_per_decode,
-                     "launches_timed": len(dec_ms)},
+                     "launches_timed": launches,
+                     "timing": "events around each timed step's 32 back-to-back layer calls, / 32 (gaps included)",
+                     "achievable": probe},
         "wall_s_timed": wall,
-        "parity_step0_layer0": parity,
+        "parity_step0": parity,
         "prefill": prefill,
         "trace": trace,
         "long_context": long_ctx,
@@ -900,6 +1093,8 @@ def main():
         "tiny_decode": tiny,
         "cpu_baseline": cpu_baseline,
     }
+    if probe and probe.get("slab_read_gb_s"):
+        rec["roofline"]["frac_of_achievable"] = achieved / probe["slab_read_gb_s"]
     print(json.dumps(rec), flush=True)
 
     if args.copy_probe_mib > 0:

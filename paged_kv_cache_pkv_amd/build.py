@@ -14,6 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
+PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")  # bandwidth probes: a measurement aid, not the product ABI
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 SOURCES = ["errors.cpp", "pool.cpp", "append.hip", "decode.hip", "prefill.hip", "blocks.hip", "fp8.hip", "prefix.hip"]
@@ -44,20 +45,26 @@ def _run(cmd, verbose):
         print("\n".join(msgs), flush=True)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (always) and link libpkv.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    cc = hipcc()
+def _link(cc, sources, lib, verbose):
     objs = []
-    for src in SOURCES:
+    for src in sources:
         path = os.path.join(CSRC, src)
         obj = os.path.join(OBJDIR, src + ".o")
         lang = ["-x", "hip"] + DEVICE if src.endswith(".hip") else ["-x", "c++"]
         _run([cc, *COMMON, *lang, "-c", path, "-o", obj], verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (always) and link libpkv.so, and the bandwidth
+    probes into libpkv_probe.so; returns libpkv.so's path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    cc = hipcc()
+    _link(cc, SOURCES, LIB, verbose)
+    _link(cc, ["probe.hip"], PROBE_LIB, verbose)
     return LIB
 
 

@@ -174,7 +174,7 @@ class ContinuousBatchTrace:
 
     # ---------------------------------------------------------------- one step
 
-    def step(self, events=None):
+    def step(self, events=None, before_decode=None):
         """Leave, join, grow, append one token per row, decode.  Returns the
         step's row snapshot (for checkers).  With events=(start, filled,
         launch, end) it records them around the fill of joining rows and
@@ -182,7 +182,9 @@ class ContinuousBatchTrace:
         (one batched table growth through the block pool, and the staging and
         asynchronous upload of tables, lengths and marks through pinned
         memory) is timed on the host and returned as snap["host_ms"]; the
-        step's synthetic inputs are drawn before it and not counted."""
+        step's synthetic inputs are drawn before it and not counted.
+        before_decode, if given, is called just before the decode part is
+        queued (e.g. to scrub the caches)."""
         torch = self.torch
         for r in self.rows:
             if r.generated >= r.answer:
@@ -227,6 +229,8 @@ class ContinuousBatchTrace:
         ev.record()
         self._stage_done[st] = ev
         host_ms = (time.perf_counter() - t_host) * 1e3
+        if before_decode is not None:
+            before_decode()
         if events:
             events[2].record()
         if self.shared_decode:

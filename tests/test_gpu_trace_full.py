@@ -49,8 +49,9 @@ def test_trace_full_size_parity(shared_decode):
             say(f"trace step {s} ({'shared-prefix' if shared_decode else 'appending'} decode): {len(snap['reqs'])} "
                 f"rows, {sharers} sharing the prefix, context {int(snap['lens'].min())}..{int(snap['lens'].max())}")
     assert max_sharers > 32, "the prefix must be shared by more rows than one tile holds"
+    # answers are U{1..1000} tokens, so over 300 steps some 15-20 rows finish and are refilled
     joins = len(tr.log["joins"])
-    assert joins > 64 + 20, "rows must leave and be refilled"
+    assert joins >= 64 + 10, "rows must leave and be refilled"
     tr.drain()
     assert tr.pool.num_free == NB
     assert all(tr.pool.ref_count(int(b)) == 0 for b in tr.prefix_ids)

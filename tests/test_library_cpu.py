@@ -400,3 +400,20 @@ def test_pool_grow_rows_matches_model():
         lib_pool.grow_rows(tables, lens, np.full(R, 16 * stride + 1))
     assert e.value.name == "INVALID_ARG"
     assert np.array_equal(tables, before[0]) and np.array_equal(lens, before[1]) and lib_pool.num_free == before[2]
+
+
+def test_probe_library_exports_its_header():
+    """The bandwidth probes (a measurement aid) export every call pkv_probe.h declares
+    and reject bad arguments before any launch."""
+    from paged_kv_cache_pkv_amd import probe
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pkv_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(pkv_probe_[a-z0-9_]+)\s*\(", text)))
+    assert names == sorted(probe.SIGNATURES)
+    L = probe.lib()
+    assert L.pkv_probe_stream_read(None, 4096, FAKE, 1, None) == -1
+    assert L.pkv_probe_stream_read(FAKE, 4100, FAKE, 1, None) == -1     # not a multiple of 16
+    assert L.pkv_probe_stream_read(FAKE, 1 << 31, FAKE, 1, None) == -1  # too large
+    assert L.pkv_probe_slab_read(FAKE, 1 << 20, FAKE, 4, 4000, FAKE, 1, None) == -1  # slab not a multiple of 4096
+    assert L.pkv_probe_slab_read(FAKE, 1 << 20, FAKE, -1, 4096, FAKE, 1, None) == -1
+    assert L.pkv_probe_slab_read(FAKE, 1 << 20, FAKE, 0, 4096, FAKE, 1, None) == 0   # nothing to read
