@@ -226,6 +226,24 @@ int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer, void* out
                                 const int32_t* context_lens, int32_t num_rows, int32_t max_context_len, float scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_decode_attention_append for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, contract and result (the same pool bytes and
+ * output bits) as pkv_decode_attention_append, without the workspace: the
+ * split-K partials go to a scratch array the library holds on each GPU it runs
+ * on, PKV_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, until the process ends.  The
+ * call allocates nothing.  A call needing more scratch than that
+ * (pkv_decode_workspace_size(cache, num_rows, max_context_len) bytes) returns
+ * PKV_ERR_WORKSPACE before anything is launched.  All calls on one GPU share
+ * its scratch array: calls whose work overlaps in time on one GPU (on
+ * different streams, or from several threads) race and give unspecified
+ * output; calls queued on one stream do not. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pkv_decode_attention_append_noalloc(const pkv_cache* cache, int32_t layer, void* out, const void* q,
+                                        const void* k_new, const void* v_new, const int32_t* block_tables,
+                                        int32_t bt_stride, const int32_t* context_lens, int32_t num_rows,
+                                        int32_t max_context_len, float scale, void* stream);
+
 /* ------------------------------------------------------------------------
  * Chunked-prefill attention mixed with decode rows in one call.
  *

@@ -256,6 +256,20 @@ def decode_attention_append_gqa(cache: PagedCache, num_q_heads: int, layer: int,
         _check(lib().pkv_decode_attention_append_gqa(ctypes.byref(cache.desc), int(num_q_heads), *args))
 
 
+def decode_attention_append_noalloc(cache: PagedCache, layer: int, out, q, k_new, v_new, block_tables, context_lens,
+                                    max_context_len: int, scale: float, stream=None):
+    """decode_attention_append with the split-K partials in the library's own
+    per-GPU scratch array (no workspace, no allocation); calls overlapping on
+    one GPU race."""
+    R, stride = (int(x) for x in block_tables.shape)
+    _rows_need(R, cache.num_heads, out=out, q=q, k_new=k_new, v_new=v_new)
+    _need(context_lens, R, "context_lens")
+    _check(lib().pkv_decode_attention_append_noalloc(
+        ctypes.byref(cache.desc), int(layer), _dptr(out, "out", 2), _dptr(q, "q", 2), _dptr(k_new, "k_new", 2),
+        _dptr(v_new, "v_new", 2), _dptr(block_tables, "block_tables", 4), stride,
+        _dptr(context_lens, "context_lens", 4), R, int(max_context_len), float(scale), _stream_ptr(stream)))
+
+
 def decode_workspace_size_prefix(cache: PagedCache, num_rows: int, max_context_len: int, prefix_blocks: int) -> int:
     return int(lib().pkv_decode_workspace_size_prefix(ctypes.byref(cache.desc), int(num_rows), int(max_context_len),
                                                       int(prefix_blocks)))

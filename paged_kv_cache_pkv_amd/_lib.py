@@ -52,6 +52,8 @@ SIGNATURES = {
     "pkv_split_tokens": (c_i32, []),
     "pkv_decode_attention_append": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
                                                    c_i32, c_i32, ctypes.c_float, c_vp, c_size, c_vp]),
+    "pkv_decode_attention_append_noalloc": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                           c_i32, c_vp, c_i32, c_i32, ctypes.c_float, c_vp]),
     "pkv_decode_attention_append_gqa": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                        c_i32, c_vp, c_i32, c_i32, ctypes.c_float, c_vp, c_size,
                                                        c_vp]),

@@ -390,3 +390,77 @@ extern "C" int pkv_decode_attention_append(const pkv_cache* cache, int32_t layer
                                          context_lens, num_rows, max_context_len, scale, workspace, workspace_bytes,
                                          stream);
 }
+
+// ---------------------------------------------------------------- no-alloc call
+//
+// pkv_decode_attention_append for callers that cannot allocate (code under HIP
+// graph capture, tight serving loops): the split-K partials live in this
+// library-owned device array instead of a caller workspace.  Each GPU holds
+// its own copy of the array until the process ends; its device address is
+// looked up once per device (the array's name is a host-side stand-in and
+// must never reach a kernel).  Calls on one GPU share the array: calls that
+// overlap in time on one GPU race.  Nothing in it needs clearing: a call
+// writes every partial it reads.
+
+#include <atomic>
+#include <mutex>
+
+namespace pkv {
+namespace {
+
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's copy of `scratch` (its device address), or null with
+// the error set.
+void* scratch_on_current_device() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(PKV_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(PKV_ERR_UNSUPPORTED, "device index beyond the library's scratch table");
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess || !p) {
+      fail(PKV_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(g));
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_decode_attention_append_noalloc(const pkv_cache* cache, int32_t layer, void* out, const void* q,
+                                                   const void* k_new, const void* v_new,
+                                                   const int32_t* block_tables, int32_t bt_stride,
+                                                   const int32_t* context_lens, int32_t num_rows,
+                                                   int32_t max_context_len, float scale, void* stream) {
+  using namespace pkv;
+  if (int rc = check_cache(cache)) return rc;
+  if (num_rows < 1 || max_context_len < 1) return fail(PKV_ERR_INVALID_ARG, "num_rows and max_context_len must be >= 1");
+  const size_t need = pkv_decode_workspace_size(cache, num_rows, max_context_len);
+  if (need > kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE, "the call needs " + std::to_string(need) +
+                                       " bytes of split-K scratch; the no-alloc call holds at most " +
+                                       std::to_string(kScratchBytes) + " (use pkv_decode_attention_append)");
+  void* ws = scratch_on_current_device();
+  if (!ws) return PKV_ERR_HIP;
+  return pkv_decode_attention_append(cache, layer, out, q, k_new, v_new, block_tables, bt_stride, context_lens,
+                                     num_rows, max_context_len, scale, ws, kScratchBytes, stream);
+}
