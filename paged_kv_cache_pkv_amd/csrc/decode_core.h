@@ -355,9 +355,48 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Up to 8 ranges, every load of a merge goes out in one round trip.
+#ifndef PKV_MERGE_FAST
+#define PKV_MERGE_FAST 1
+#endif
+
 __device__ __forceinline__ void merge_partials(const float* __restrict__ part_o, const float2* __restrict__ ml,
                                                int nsplit, uint32_t* __restrict__ out_head) {
   const int lane = threadIdx.x & 63;
+#if PKV_MERGE_FAST
+  if (nsplit <= 8) {
+    // Up to 8 ranges: every statistic and partial load goes out in one round
+    // trip (none depends on the maximum); the arithmetic below is the general
+    // path's, in the same order, so the bits are the same.
+    const float2* pf = reinterpret_cast<const float2*>(part_o) + lane;
+    const float2 mine = lane < nsplit ? ml[lane] : make_float2(kMinusBig, 0.0f);
+    float2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = u < nsplit ? pf[(size_t)u * (kHeadDim / 2)] : make_float2(0.0f, 0.0f);
+    const float M = wave_max(mine.x);
+    const float w_mine = fast_exp2(mine.x - M);
+    float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < nsplit) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), u));
+        o0 = fmaf(p[u].x, w, o0);
+        o1 = fmaf(p[u].y, w, o1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < nsplit) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), u));
+        const float ls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.y), u));
+        l = fmaf(ls, w, l);
+      }
+    }
+    const float inv = 1.0f / l;
+    out_head[lane] = pack_half2(o0 * inv, o1 * inv);
+    return;
+  }
+#endif
   const float2* po = reinterpret_cast<const float2*>(part_o) + lane;
   float M = kMinusBig;
   for (int s0 = 0; s0 < nsplit; s0 += 64) {

@@ -43,8 +43,11 @@ constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kQPerWave = 32;
 constexpr int kBQ = kPrefillWaves * kQPerWave;  // queries per tile
 constexpr int kBK = 64;                         // keys per step
+// Order of the mixed launch: -1 lets the host decide per call (see the
+// launch), 0 puts every prefill tile first, 1 spreads the tiles among the
+// decode workgroups.
 #ifndef PKV_PREFILL_INTERLEAVE
-#define PKV_PREFILL_INTERLEAVE 0
+#define PKV_PREFILL_INTERLEAVE -1
 #endif
 #ifndef PKV_PREFILL_SPLIT
 #define PKV_PREFILL_SPLIT 2048
@@ -100,6 +103,7 @@ struct PrefillArgs {
   int tiles_max, ranges_max;   // prefill grid factors
   int prefill_wgs;             // prefill tile workgroups (a multiple of kXcds)
   int decode_wgs;              // decode workgroups (a multiple of kXcds)
+  int interleave;              // spread the prefill tiles among the decode workgroups
   float qk_scale;              // scale * log2(e)
 };
 
@@ -501,13 +505,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
   const int np = a.prefill_wgs / kXcds;
   const int nd = a.decode_wgs / kXcds;
   const int tot = np + nd;
-#if PKV_PREFILL_INTERLEAVE
-  const int before = (int)((long long)m * np / tot);     // prefill positions before m
-  const int upto = (int)((long long)(m + 1) * np / tot);
-#else
-  const int before = m < np ? m : np;  // all of an XCD's prefill tiles first
-  const int upto = m < np ? m + 1 : np;
-#endif
+  int before, upto;
+  if (a.interleave) {
+    before = (int)((long long)m * np / tot);  // prefill positions before m
+    upto = (int)((long long)(m + 1) * np / tot);
+  } else {
+    before = m < np ? m : np;  // all of an XCD's prefill tiles first
+    upto = m < np ? m + 1 : np;
+  }
   if (upto > before) {
     const int logical = x * np + before;
     const int tile = logical % a.tiles_max;
@@ -669,6 +674,14 @@ extern "C" int pkv_chunked_prefill_attention_gqa(const pkv_cache* cache, int32_t
   a.ranges_max = (int)ranges;
   a.prefill_wgs = (int)pre;
   a.decode_wgs = (int)dec;
+  // Spreading the tiles among the decode workgroups lets a CU hold a tile and
+  // a decode workgroup at once, which pays when the batch has decode rows;
+  // with none, the empty decode slots only scatter the tiles.  The host knows
+  // no row's query count, but a batch whose rows are more than
+  // ceil(total_q / max_q_per_row) cannot be all full-size chunks.  The choice
+  // changes only the order of workgroups, never a result.
+  const int64_t full_rows = ((int64_t)total_q + max_q_per_row - 1) / max_q_per_row;
+  a.interleave = PKV_PREFILL_INTERLEAVE >= 0 ? PKV_PREFILL_INTERLEAVE : (num_rows > full_rows ? 1 : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   prefill_mixed_kernel<<<dim3((unsigned)(pre + dec)), dim3(kPrefillThreads), 0, s>>>(a);
   if (int rc = check_launch("prefill mixed kernel")) return rc;
