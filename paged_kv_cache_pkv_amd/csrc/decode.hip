@@ -113,18 +113,31 @@ __global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_ke
 // through LDS in wave order (The inference engine, wpnews.pro: tile
 // statistics combine exactly).  The range partition matches the decode
 // launch's, so a row's result does not depend on its batch neighbours.
-#ifndef PKV_GQA_WAVES
-#define PKV_GQA_WAVES 4
+// Waves per workgroup by group size (each takes 16 / waves blocks of a range).
+#ifndef PKV_GQA_WAVES2
+#define PKV_GQA_WAVES2 2
+#endif
+#ifndef PKV_GQA_WAVES4
+#define PKV_GQA_WAVES4 2
+#endif
+#ifndef PKV_GQA_WAVES8
+#define PKV_GQA_WAVES8 2
 #endif
 #ifndef PKV_GQA_DEPTH
 #define PKV_GQA_DEPTH 3
 #endif
-constexpr int kGqaWaves = PKV_GQA_WAVES;
-constexpr int kGqaThreads = 64 * kGqaWaves;
-static_assert(kSplitBlocks % kGqaWaves == 0, "each wave takes an equal share of a range");
+#ifndef PKV_GQA_DEPTH8
+#define PKV_GQA_DEPTH8 2
+#endif
+template <int G>
+constexpr int gqa_waves() {
+  return G <= 2 ? PKV_GQA_WAVES2 : G <= 4 ? PKV_GQA_WAVES4 : PKV_GQA_WAVES8;
+}
 
 template <int G, bool kAppend>
-__global__ __launch_bounds__(kGqaThreads) void decode_gqa_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * gqa_waves<G>()) void decode_gqa_kernel(DecodeArgs a) {
+  constexpr int kGqaWaves = gqa_waves<G>();
+  static_assert(kSplitBlocks % kGqaWaves == 0, "each wave takes an equal share of a range");
   __shared__ float s_m[kGqaWaves][G], s_l[kGqaWaves][G];
   __shared__ float4 s_o[kGqaWaves][G][32];
   const int n = blockIdx.x;
@@ -168,7 +181,7 @@ __global__ __launch_bounds__(kGqaThreads) void decode_gqa_kernel(DecodeArgs a) {
       new_v = a.v_new + ((size_t)r * a.num_heads + h) * 16;
     }
   }
-  fold_blocks<(G >= 8 ? 2 : PKV_GQA_DEPTH), G>(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
+  fold_blocks<(G >= 8 ? PKV_GQA_DEPTH8 : PKV_GQA_DEPTH), G>(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
                                         a.block_tables + (size_t)r * a.bt_stride, L, b0, b1, a.q + rh * 16,
                                         a.qk_scale, st, new_k, new_v);
 #pragma unroll
@@ -331,18 +344,18 @@ int decode_launch(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, vo
   } else {
     const int64_t wgs = rs_total * cache->num_heads;
     if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-    const dim3 grid((unsigned)wgs), block(kGqaThreads);
+    const dim3 grid((unsigned)wgs);
     if (k_new) {
       switch (G) {
-        case 2: decode_gqa_kernel<2, true><<<grid, block, 0, s>>>(a); break;
-        case 4: decode_gqa_kernel<4, true><<<grid, block, 0, s>>>(a); break;
-        default: decode_gqa_kernel<8, true><<<grid, block, 0, s>>>(a); break;
+        case 2: decode_gqa_kernel<2, true><<<grid, dim3(64 * gqa_waves<2>()), 0, s>>>(a); break;
+        case 4: decode_gqa_kernel<4, true><<<grid, dim3(64 * gqa_waves<4>()), 0, s>>>(a); break;
+        default: decode_gqa_kernel<8, true><<<grid, dim3(64 * gqa_waves<8>()), 0, s>>>(a); break;
       }
     } else {
       switch (G) {
-        case 2: decode_gqa_kernel<2, false><<<grid, block, 0, s>>>(a); break;
-        case 4: decode_gqa_kernel<4, false><<<grid, block, 0, s>>>(a); break;
-        default: decode_gqa_kernel<8, false><<<grid, block, 0, s>>>(a); break;
+        case 2: decode_gqa_kernel<2, false><<<grid, dim3(64 * gqa_waves<2>()), 0, s>>>(a); break;
+        case 4: decode_gqa_kernel<4, false><<<grid, dim3(64 * gqa_waves<4>()), 0, s>>>(a); break;
+        default: decode_gqa_kernel<8, false><<<grid, dim3(64 * gqa_waves<8>()), 0, s>>>(a); break;
       }
     }
   }
