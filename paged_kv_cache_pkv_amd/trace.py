@@ -101,15 +101,13 @@ class ContinuousBatchTrace:
         else:
             ws = decode_workspace_size(self.cache, max_rows, max_ctx)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
-        # step metadata: a ring of pinned host buffers, copied asynchronously
-        # into device arrays that every step reuses
+        # step metadata: a ring of pinned host buffers, each step's tables,
+        # lengths, positions and marks copied asynchronously in one transfer
+        # into one device array that every step reuses
         n_meta = max_rows * self.stride + 3 * max_rows
         self._stage = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(self.STAGES)]
         self._stage_done = [None] * self.STAGES
-        self.tab_d = torch.empty((max_rows, self.stride), dtype=torch.int32, device=self.dev)
-        self.lens_d = torch.empty(max_rows, dtype=torch.int32, device=self.dev)
-        self.pos_d = torch.empty(max_rows, dtype=torch.int32, device=self.dev)
-        self.marks_d = torch.empty(max_rows, dtype=torch.int32, device=self.dev)
+        self.meta_d = torch.empty(n_meta, dtype=torch.int32, device=self.dev)
         self.rot_d = torch.arange(max_rows, dtype=torch.int32, device=self.dev)
         self.log = {"prefix_ids": self.prefix_ids.copy(), "joins": [], "steps": []}
 
@@ -219,12 +217,13 @@ class ContinuousBatchTrace:
         a[n_tab:n_tab + R] = lens
         a[n_tab + R:n_tab + 2 * R] = lens - 1
         a[n_tab + 2 * R:n_tab + 3 * R] = [1 if r.shared else 0 for r in rows]
-        tab_d, lens_d, pos_d = self.tab_d[:R], self.lens_d[:R], self.pos_d[:R]
-        marks_d, rot_d = self.marks_d[:R], self.rot_d[:R]
-        tab_d.copy_(buf[:n_tab].view(R, self.stride), non_blocking=True)
-        lens_d.copy_(buf[n_tab:n_tab + R], non_blocking=True)
-        pos_d.copy_(buf[n_tab + R:n_tab + 2 * R], non_blocking=True)
-        marks_d.copy_(buf[n_tab + 2 * R:n_tab + 3 * R], non_blocking=True)
+        n = n_tab + 3 * R
+        self.meta_d[:n].copy_(buf[:n], non_blocking=True)
+        tab_d = self.meta_d[:n_tab].view(R, self.stride)
+        lens_d = self.meta_d[n_tab:n_tab + R]
+        pos_d = self.meta_d[n_tab + R:n_tab + 2 * R]
+        marks_d = self.meta_d[n_tab + 2 * R:n]
+        rot_d = self.rot_d[:R]
         ev = torch.cuda.Event()
         ev.record()
         self._stage_done[st] = ev
