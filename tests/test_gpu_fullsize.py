@@ -31,7 +31,8 @@ class Blocks:
         return self.slab[self.index[int(b)]]
 
 
-def _run(batch, layers, seed):
+def _run(batch, layers, seed, all_layer_rows=()):
+    """Check every row of `layers`, and every layer of the rows in `all_layer_rows`."""
     torch = torch_cuda()
     dev = torch.device("cuda", 0)
     pool = torch.empty((NB, NL, 2, H, 16, D), dtype=torch.int16, device=dev)
@@ -41,6 +42,11 @@ def _run(batch, layers, seed):
     ids = np.unique(np.concatenate([batch.block_tables[r, :nblk[r]] for r in range(R)]))
     ids_d = torch.from_numpy(ids.astype(np.int64)).to(dev)
     before = {l: pool[ids_d, l].cpu().numpy().view(np.uint16) for l in layers}
+    # the few rows checked on every layer: their own blocks, all layers
+    row_ids = np.unique(np.concatenate([batch.block_tables[r, :nblk[r]] for r in all_layer_rows])) if all_layer_rows \
+        else np.zeros(0, dtype=np.int32)
+    row_slab = pool[torch.from_numpy(row_ids.astype(np.int64)).to(dev)].cpu().numpy().view(np.uint16) \
+        if all_layer_rows else None
     cache = pkv.PagedCache(pool)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
     tables, lens, pos = t(batch.block_tables), t(batch.context_lens), t(batch.positions)
@@ -69,6 +75,17 @@ def _run(batch, layers, seed):
         ref = opaged.decode(Blocks(ids, slab), batch.q[l], batch.block_tables, batch.context_lens, SCALE)
         s = assert_close(got[l], ref, f"{batch.name} layer {l}")
         say(f"  {batch.name} layer {l}: {s}")
+    for r in all_layer_rows:
+        for l in range(NL):
+            slab = row_slab[:, l].copy()
+            index = {int(b): i for i, b in enumerate(row_ids)}
+            b, s = opaged.locate(batch.block_tables[r], int(batch.positions[r]))
+            slab[index[b], 0, :, s, :] = batch.k_new[l, r]
+            slab[index[b], 1, :, s, :] = batch.v_new[l, r]
+            ref = opaged.decode(Blocks(row_ids, slab), batch.q[l], batch.block_tables, batch.context_lens, SCALE,
+                                rows=[r])[0]
+            assert_close(got[l, r], ref, f"{batch.name} row {r} layer {l}")
+        say(f"  {batch.name} row {r} (context {int(batch.context_lens[r])}): all {NL} layers within tolerance")
     del pool
     torch.cuda.empty_cache()
 
@@ -76,7 +93,8 @@ def _run(batch, layers, seed):
 def test_average_mix_full_pool():
     b = c2_average_mix(seed=1)
     say(f"{b.name}: sum context {int(b.context_lens.sum())}")
-    _run(b, layers=(0, 31), seed=1001)
+    longest = int(np.argmax(b.context_lens))
+    _run(b, layers=(0, 31), seed=1001, all_layer_rows=(0, longest))
 
 
 def test_long_context_full_pool():
