@@ -189,6 +189,7 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
     tflops = flops / (chunk_ms / 1e3) / 1e12
     rec = counted_record(PREFILL_COUNTERS, PREFILL_SOURCES)
     prefill_traffic = rec.get("traffic_bytes_per_launch") if rec else None
+    ceiling = measure_mfma_ceiling(torch, stream)
     return {
         "workload": "512-token causal chunk at offset 7488 of an 8000-token prompt + 31 average-mix decode rows, "
                     "one layer, 32 heads x 128, FP16",
@@ -202,7 +203,9 @@ def measure_prefill(torch, pkv, dev, stream, reps=20):
         "append_bulk_roofline": appends,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": prefill_traffic,
-                     "kernel": "pkv_chunked_prefill_attention on the chunk alone (tile + merge launches)"},
+                     "kernel": "pkv_chunked_prefill_attention on the chunk alone (tile + merge launches)",
+                     "achievable": ceiling,
+                     "frac_of_achievable": tflops / ceiling["mfma_f16_tflops"] if ceiling else None},
     }
 
 
@@ -386,6 +389,26 @@ def measure_bandwidth(torch, pkv, cache, tables, tlen, stream):
         "stream_read_gb_s": ((1 << 31) - 4096) / (stream_nt / 1e3) / 1e9,
         "stream_read_plain_gb_s": ((1 << 31) - 4096) / (stream_pl / 1e3) / 1e9,
     }
+
+
+def measure_mfma_ceiling(torch, stream, iters=4000, reps=5):
+    """Sustained FP16 matrix-core rate on this machine, from the probe in
+    libpkv_probe.so: every SIMD kept busy with independent
+    v_mfma_f32_32x32x16_f16 chains for about a millisecond per launch, the
+    clock settling where sustained matrix work holds it."""
+    from paged_kv_cache_pkv_amd import probe
+
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe.mfma_f16(iters, sink, stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    flops = sum(probe.mfma_f16(iters, sink, stream) for _ in range(reps))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"probe": "libpkv_probe.so pkv_probe_mfma_f16 (include/pkv_probe.h)",
+            "mfma_f16_tflops": flops / (e0.elapsed_time(e1) / 1e3) / 1e12,
+            "note": f"{reps} launches of {iters} rounds of 4 independent MFMA chains per wave, 16 waves per CU"}
 
 
 def measure_block_copies(torch, pkv, cache, free_ids, stream, n=64, reps=10):

@@ -1,14 +1,17 @@
 /*
- * pkv_probe.h - bandwidth probes for MI355X (gfx950): a measurement aid built
- * beside libpkv.so into libpkv_probe.so.  Not part of the paged-attention
- * interface in pkv.h; nothing in libpkv.so calls these.
+ * pkv_probe.h - bandwidth and matrix-core probes for MI355X (gfx950): a
+ * measurement aid built beside libpkv.so into libpkv_probe.so.  Not part of
+ * the paged-attention interface in pkv.h; nothing in libpkv.so calls these.
  *
  * They measure the read bandwidth a memory-bound kernel can reach on the box,
  * the ceiling against which the decode kernels' achieved bandwidth is read
  * (Inference Infrastructure, seeitflow.com: after "Three iterations with the
  * state written out", reading the KV cache at the memory bandwidth sets the
- * decode step's floor).  Every load's result feeds a comparison whose store
- * (to sink[0]) essentially never happens, so no load can be dropped.
+ * decode step's floor), and the FP16 matrix-core rate a kernel sustains, the
+ * ceiling of the prefill tile's matrix products (The inference engine,
+ * wpnews.pro, "Prefill and decode ask the accelerator for different work").
+ * Every result feeds a comparison whose store (to sink[0]) essentially never
+ * happens, so no load or product can be dropped.
  *
  * Return value: 0, or -1 for an invalid argument (nothing launched), or -7
  * when the HIP runtime refuses the launch.  All pointers are device pointers
@@ -40,6 +43,14 @@ int pkv_probe_stream_read(const void* src, size_t nbytes, uint32_t* sink, int no
  * below 2^31; base 16-byte aligned. */
 int pkv_probe_slab_read(const void* base, size_t base_bytes, const int32_t* slab_index, int32_t n, size_t slab_bytes,
                         uint32_t* sink, int nontemporal, void* stream);
+
+/* Sustained FP16 matrix-core rate: 4 workgroups of 4 waves per compute unit,
+ * each wave running `iters` rounds of four independent
+ * v_mfma_f32_32x32x16_f16 chains (operands in registers, nothing read from
+ * memory).  *flops (host pointer) receives the launch's floating-point
+ * operations, 2 * 32 * 32 * 16 per product; divide by the launch's time.
+ * iters must be in [1, 2^24]. */
+int pkv_probe_mfma_f16(int32_t iters, uint32_t* sink, double* flops, void* stream);
 
 #ifdef __cplusplus
 }

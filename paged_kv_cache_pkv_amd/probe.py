@@ -1,5 +1,6 @@
-"""Binding of libpkv_probe.so (include/pkv_probe.h): read-bandwidth probes, a
-measurement aid beside the library.  Argument marshalling only."""
+"""Binding of libpkv_probe.so (include/pkv_probe.h): read-bandwidth and
+matrix-core probes, a measurement aid beside the library.  Argument
+marshalling only."""
 from __future__ import annotations
 
 import ctypes
@@ -13,6 +14,8 @@ SIGNATURES = {
                                              ctypes.c_void_p]),
     "pkv_probe_slab_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
+    "pkv_probe_mfma_f16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.c_void_p]),
 }
 _lib = None
 
@@ -46,3 +49,11 @@ def slab_read(base, slab_index, slab_bytes, sink, nontemporal=True, stream=None)
     _ok(lib().pkv_probe_slab_read(ctypes.c_void_p(base.data_ptr()), base.numel() * base.element_size(),
                                   ctypes.c_void_p(slab_index.data_ptr()), int(slab_index.numel()), int(slab_bytes),
                                   ctypes.c_void_p(sink.data_ptr()), int(bool(nontemporal)), _stream_ptr(stream)))
+
+
+def mfma_f16(iters, sink, stream=None):
+    """Queue the matrix-core probe; returns the launch's floating-point operations."""
+    flops = ctypes.c_double(0.0)
+    _ok(lib().pkv_probe_mfma_f16(int(iters), ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flops),
+                                 _stream_ptr(stream)))
+    return flops.value

@@ -33,6 +33,7 @@ def test_bench_runs_every_leg():
     for leg in ("prefill", "trace", "long_context", "gqa_decode", "fp8_decode", "block_copy", "tiny_decode"):
         assert rec[leg], leg
     assert 0 < rec["prefill"]["roofline"]["frac"] < 1
+    assert 0 < rec["prefill"]["roofline"]["frac_of_achievable"] < 1
     assert rec["trace"]["steps"] == 12 and rec["trace"]["pool_drained"]
     assert rec["parity_step0"]["pass"], rec["parity_step0"]
     cb = rec["cpu_baseline"]

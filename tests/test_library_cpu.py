@@ -403,7 +403,7 @@ def test_pool_grow_rows_matches_model():
 
 
 def test_probe_library_exports_its_header():
-    """The bandwidth probes (a measurement aid) export every call pkv_probe.h declares
+    """The bandwidth and matrix-core probes (a measurement aid) export every call pkv_probe.h declares
     and reject bad arguments before any launch."""
     from paged_kv_cache_pkv_amd import probe
 
@@ -417,3 +417,8 @@ def test_probe_library_exports_its_header():
     assert L.pkv_probe_slab_read(FAKE, 1 << 20, FAKE, 4, 4000, FAKE, 1, None) == -1  # slab not a multiple of 4096
     assert L.pkv_probe_slab_read(FAKE, 1 << 20, FAKE, -1, 4096, FAKE, 1, None) == -1
     assert L.pkv_probe_slab_read(FAKE, 1 << 20, FAKE, 0, 4096, FAKE, 1, None) == 0   # nothing to read
+    flops = ctypes.c_double(0.0)
+    assert L.pkv_probe_mfma_f16(0, FAKE, ctypes.byref(flops), None) == -1        # no rounds
+    assert L.pkv_probe_mfma_f16((1 << 24) + 1, FAKE, ctypes.byref(flops), None) == -1
+    assert L.pkv_probe_mfma_f16(10, None, ctypes.byref(flops), None) == -1
+    assert L.pkv_probe_mfma_f16(10, FAKE, None, None) == -1
