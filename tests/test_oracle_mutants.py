@@ -67,6 +67,43 @@ def _group_kv_tiled(K, V, group):
     return np.tile(K, (group, 1, 1)), np.tile(V, (group, 1, 1))
 
 
+_chunked = paged.chunked_prefill
+
+
+def _chunk_positions_late(pool_layer, q, query_start, block_tables, context_lens, scale, rows=None, group=1):
+    """Each chunk query placed one position later: it sees one key past its own."""
+    qs = np.asarray(query_start)
+    outs = []
+    for r in (range(len(context_lens)) if rows is None else rows):
+        L = int(context_lens[r])
+        a, b = int(qs[r]), int(qs[r + 1])
+        K, V = paged.group_kv(*paged.gather_kv(pool_layer, block_tables[r], L), group)
+        pos = np.minimum(np.arange(L - (b - a), L) + 1, L - 1)
+        outs.append(paged.attention(np.asarray(q)[a:b], K, V, pos, scale))
+    return np.concatenate(outs, axis=0)
+
+
+def _chunk_first_query_shifted(pool_layer, q, query_start, block_tables, context_lens, scale, rows=None, group=1):
+    """The row's queries read one slot late in the flat token list (off-by-one on query_start)."""
+    qs = np.asarray(query_start).copy()
+    qs[1:-1] += 1
+    qs = np.minimum(qs, len(q))
+    return _chunked(pool_layer, q, qs, block_tables, context_lens, scale, rows, group) if np.all(np.diff(qs) >= 1) \
+        else _chunked(pool_layer, np.roll(q, 1, axis=0), query_start, block_tables, context_lens, scale, rows, group)
+
+
+def _decode_drops_last(pool_layer, q, block_tables, context_lens, scale, rows=None, group=1):
+    """Decode over one token fewer than the row holds (the appended token left out)."""
+    lens = np.maximum(np.asarray(context_lens) - 1, 1)
+    rows = range(len(context_lens)) if rows is None else rows
+    outs = []
+    for r in rows:
+        L = int(lens[r])
+        K, V = paged.group_kv(*paged.gather_kv(pool_layer, block_tables[r], L), group)
+        outs.append(paged.attention(np.asarray(q)[r:r + 1], K, V, [L - 1], scale)[0])
+    return np.stack(outs)
+
+
 def _blocks_floor(n, block_size=16):
     return int(n) // block_size
 
@@ -80,6 +117,9 @@ MUTANTS = [
     ("gather_kv", _gather_drop_tail),
     ("locate", _locate_swapped),
     ("group_kv", _group_kv_tiled),
+    ("chunked_prefill", _chunk_positions_late),
+    ("chunked_prefill", _chunk_first_query_shifted),
+    ("decode", _decode_drops_last),
 ]
 
 
