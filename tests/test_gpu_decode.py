@@ -60,6 +60,8 @@ CASES = [
     ("beyond-64-ranges", 2, 1, [20000, 16400, 16385, 7]),
     # the most heads the library accepts (32 workgroups of 4 heads per range)
     ("max-heads", 128, 2, [300, 17, 1]),
+    # many rows of mixed lengths (one and several ranges)
+    ("many-rows", 4, 1, [int(x) for x in np.random.default_rng(77).integers(1, 900, 700)]),
 ]
 
 

@@ -38,6 +38,14 @@ def oracle_prefill(b, layer=0):
     return opaged.chunked_prefill(pool[:, layer], b.q[layer], b.query_start, b.block_tables, b.context_lens, SCALE)
 
 
+def _many_rows(n):
+    """n rows of seeded lengths in [2, 1500); about a quarter are decode rows (one query), the rest chunks of up to
+    300 queries."""
+    lens = np.random.default_rng(78).integers(2, 1500, n)
+    want = np.random.default_rng(79).integers(-60, 300, n)
+    return [int(L) for L in lens], [int(max(1, min(w, L))) for w, L in zip(want, lens)]
+
+
 CASES = [
     # name, heads, lens, q_counts
     ("chunk-and-decode", 32, [700, 40, 300, 17], [300, 1, 1, 1]),
@@ -48,6 +56,8 @@ CASES = [
     ("long-rows", 2, [17000, 18200, 600], [1, 140, 300]),
     # the most KV heads the pool accepts
     ("max-heads", 128, [300, 40], [70, 1]),
+    # more rows than one wave's lanes: the tile search and the decode rows step through rows 64 at a time
+    ("many-rows", 4, *_many_rows(150)),
 ]
 
 
