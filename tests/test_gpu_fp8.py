@@ -62,6 +62,8 @@ CASES = [
     ("odd-heads", 5, 1, [300, 1, 700]),
     # the most heads the library accepts
     ("max-heads", 128, 1, [300, 17]),
+    # many rows of mixed lengths
+    ("many-rows", 4, 1, [int(x) for x in np.random.default_rng(81).integers(1, 900, 500)]),
 ]
 
 

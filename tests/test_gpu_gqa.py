@@ -80,6 +80,21 @@ def test_gqa_decode_odd_kv_heads():
     assert_close(host_f64(got), ref, f"G={G} Hkv={Hkv}")
 
 
+def test_gqa_decode_many_rows():
+    """500 rows of mixed lengths, 2 KV heads of 4 query heads each."""
+    torch = torch_cuda()
+    G, Hkv = 4, 2
+    lens = [int(x) for x in np.random.default_rng(82).integers(1, 900, 500)]
+    b = build_batch("gqa-many", 48, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 4,
+                    num_heads=Hkv, stride=max(-(-L // 16) for L in lens))
+    q = _queries(49, len(lens), Hkv * G)
+    pool = _full_pool(b)
+    say(f"gqa decode many rows: {len(lens)}")
+    got = _decode(torch, pool, Hkv * G, 0, q, b.block_tables, b.context_lens)
+    ref = opaged.decode(pool[:, 0], q, b.block_tables, b.context_lens, SCALE, group=G)
+    assert_close(host_f64(got), ref, "gqa many rows")
+
+
 def test_gqa_decode_beyond_64_ranges():
     """Grouped decode (G = 4) over rows of 79 and 65 ranges: the merge takes its
     ranges in several passes of 64."""
