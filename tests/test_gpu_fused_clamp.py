@@ -1,10 +1,11 @@
-"""The fused append + decode calls with a row longer than max_context_len.
+"""The fused append + decode calls with a row longer than max_context_len and a
+row of length 0.
 
-Such a row breaks the call's length contract: it is read clamped (for memory
-safety) and its output is unspecified, but it must append nothing -- its new
-token's slot lies past the clamp, and writing the token anywhere else would
-overwrite a cached token of that row.  Every other row appends and decodes as
-usual.  For the FP16 call, the grouped-query call (4 query heads per KV head)
+Such rows break the call's length contract: they are read clamped (for memory
+safety) and their output is unspecified, but they must append nothing -- the
+long row's new token slot lies past the clamp, and writing the token anywhere
+else would overwrite a cached token of that row; the empty row has no slot at
+all.  Every other row appends and decodes as usual.  For the FP16 call, the grouped-query call (4 query heads per KV head)
 and the 8-bit call: the pool (codes and scales) must equal the oracle's append
 of the in-contract rows alone, byte for byte over the whole pool, and the
 in-contract rows' outputs must match the oracle."""
@@ -23,7 +24,8 @@ pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarnin
 LENS = [40, 300, 601, 600, 17]  # row 2 ends one token past max_context_len
 MAXL = 600
 OVER = 2
-KEEP = [r for r in range(len(LENS)) if r != OVER]
+EMPTY = 4  # passed to the call with context length 0
+KEEP = [r for r in range(len(LENS)) if r not in (OVER, EMPTY)]
 
 
 def _batch(heads, seed):
@@ -49,10 +51,12 @@ def test_fused_append_skips_row_past_max_context_len(kind):
     R = len(LENS)
     rng = np.random.default_rng(90 + G)
     q = rng.standard_normal((R, Hq, 128), dtype=np.float32).astype(np.float16).view(np.uint16)
-    tables, lens_d = dev(b.block_tables, torch), dev(b.context_lens, torch)
+    lens_call = b.context_lens.copy()
+    lens_call[EMPTY] = 0
+    tables, lens_d = dev(b.block_tables, torch), dev(lens_call, torch)
     k, v = dev(b.k_new[layer], torch), dev(b.v_new[layer], torch)
     out = torch.empty((R, Hq, 128), dtype=torch.float16, device="cuda")
-    say(f"fused append with row {OVER} at {LENS[OVER]} > max_context_len {MAXL} ({kind})")
+    say(f"fused append with row {OVER} at {LENS[OVER]} > max_context_len {MAXL} and row {EMPTY} empty ({kind})")
     want_pool = _append_kept(b, layer)
     if kind == "fp8":
         codes, scales = ofp8.quantize_rows(b.pool)
