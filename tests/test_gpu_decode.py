@@ -41,6 +41,19 @@ def oracle_decode(batch, layer=0):
     return opaged.decode(pool[:, layer], batch.q[layer], batch.block_tables, batch.context_lens, SCALE)
 
 
+def test_decode_full_tables():
+    """Block tables exactly as long as the longest row needs (max_context_len =
+    16 * bt_stride): the last table entry is read, and nothing past it."""
+    torch = torch_cuda()
+    lens = [1024, 16, 1023, 257]
+    b = build_batch("full-tables", 33, lens, np.ones(len(lens)), num_blocks=sum(-(-L // 16) for L in lens) + 4,
+                    num_layers=1, num_heads=8, stride=64)
+    assert b.block_tables.shape[1] * 16 == max(lens)
+    say(f"decode with full tables lens={lens}")
+    got, _ = gpu_decode(b, torch)
+    say(f"  {assert_close(got, oracle_decode(b), 'full tables')}")
+
+
 def test_decode_tiny():
     torch = torch_cuda()
     b = c1_tiny()

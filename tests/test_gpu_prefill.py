@@ -59,6 +59,18 @@ CASES = [
     # more rows than one wave's lanes: the tile search and the decode rows step through rows 64 at a time
     ("many-rows", 4, *_many_rows(150)),
 ]
+# block tables exactly as long as the longest row needs (max_context_len = 16 * bt_stride)
+FULL_TABLE = ("full-tables", 8, [2048, 1000, 2047], [256, 1, 2047])
+
+
+def test_prefill_full_tables():
+    torch = torch_cuda()
+    name, heads, lens, qc = FULL_TABLE
+    b = build_batch(name, 301, lens, qc, num_blocks=sum(-(-L // 16) for L in lens) + 4, num_heads=heads, stride=128)
+    assert b.block_tables.shape[1] * 16 == max(lens)
+    say(f"prefill {name} lens={lens} q={qc}")
+    got, _ = gpu_prefill(b, torch)
+    say(f"  {assert_close(got, oracle_prefill(b), name)}")
 
 
 @pytest.mark.parametrize("name,heads,lens,qc", CASES, ids=[c[0] for c in CASES])
