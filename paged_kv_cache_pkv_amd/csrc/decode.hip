@@ -13,34 +13,32 @@
 // written directly.  Ranges depend only on the row's own length, so a row's
 // output is independent of its batch neighbours.
 //
-// Mapping onto gfx950.  One wave64 owns one (row, head, range).  A 16-token
-// block of one head is 4 KiB of keys followed (128 KiB later) by 4 KiB of
-// values, stored [token][128].  Lane l works on dims 8*(l%16) .. +7 of tokens
-// l/16, l/16 + 4, l/16 + 8, l/16 + 12: every load instruction moves four
-// whole 256-byte token rows (1 KiB contiguous per wave), straight into
-// registers -- each lane consumes exactly what it loads, so no LDS staging is
-// needed.  Loads carry the non-temporal cache policy.  Scores are dot products of FP16 pairs accumulated in fp32
-// (v_dot2_f32_f16), summed over the 16 lanes of a token with DPP moves.  Each
-// group of 16 lanes keeps its own online-softmax state over its four tokens
-// of every block; the four groups merge once at the end of the range.  Blocks
-// are software-pipelined three ahead so a wave keeps 32 KiB in flight.
+// Mapping onto gfx950.  A workgroup of 4 waves owns one (row, head, range);
+// wave w folds the range's w-th quarter (4 of its 16 blocks) and the waves
+// combine their softmax states through LDS.  A 16-token block of one head is
+// 4 KiB of keys followed (128 KiB later) by 4 KiB of values, stored
+// [token][128].  Lane l works on dims 8*(l%16) .. +7 of tokens l/16, l/16 + 4,
+// l/16 + 8, l/16 + 12: every load instruction moves four whole 256-byte token
+// rows (1 KiB contiguous per wave), straight into registers -- each lane
+// consumes exactly what it loads, so no LDS staging is needed.  Loads carry
+// the non-temporal cache policy.  Scores are dot products of FP16 pairs
+// accumulated in fp32 (v_dot2_f32_f16), summed over the 16 lanes of a token
+// with DPP moves.  Each group of 16 lanes keeps its own online-softmax state
+// over its four tokens of every block; the four groups merge at the end of the
+// wave's share.  Blocks are software-pipelined two ahead.  Short shares keep
+// many independent waves in flight, so the launch fills and drains faster
+// than with one wave walking a whole range.
 
 #include "decode_core.h"
 
 namespace pkv {
 namespace {
 
-#ifndef PKV_WAVES
-#define PKV_WAVES 4
-#endif
 #ifndef PKV_XCD_REMAP
 #define PKV_XCD_REMAP 1
 #endif
-#ifndef PKV_MIN_WAVES
-#define PKV_MIN_WAVES 1
-#endif
 
-constexpr int kWavesPerGroup = PKV_WAVES;  // heads per workgroup
+constexpr int kWavesPerGroup = 4;  // heads per merge workgroup
 constexpr int kDecodeThreads = 64 * kWavesPerGroup;
 constexpr int kXcds = 8;
 
@@ -63,47 +61,44 @@ struct DecodeArgs {
 // kAppend: each row's new token (position L - 1) comes from k_new / v_new and
 // the range holding it also writes it into its pool slot (the step's append).
 template <bool kAppend>
-__global__ __launch_bounds__(kDecodeThreads, PKV_MIN_WAVES) void decode_split_kernel(DecodeArgs a) {
-  // 1-D grid over (row, range, group of kWavesPerGroup heads).  Workgroups go
-  // to the XCDs round-robin by index; with the remap, the head groups of one
-  // (row, range) land on one XCD back to back, so they share its L2 and TLB
-  // for the same block slabs.
-  const int head_groups = (a.num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+__global__ __launch_bounds__(64 * kRangeWaves) void decode_kernel(DecodeArgs a) {
+  __shared__ RangeScratch lds;
+  // 1-D grid over (row, range, head).  Workgroups go to the XCDs round-robin
+  // by index; with the remap, the heads of one (row, range) land on one XCD
+  // back to back, so they share its L2 and TLB for the same block slabs.
   const int n = blockIdx.x;
 #if PKV_XCD_REMAP
   const int m = n / kXcds;
-  const int hg = m % head_groups;
-  const int rs = (n % kXcds) + kXcds * (m / head_groups);
+  const int h = m % a.num_heads;
+  const int rs = (n % kXcds) + kXcds * (m / a.num_heads);
 #else
-  const int hg = n % head_groups;
-  const int rs = n / head_groups;
+  const int h = n % a.num_heads;
+  const int rs = n / a.num_heads;
 #endif
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
-  // wave-uniform: lets every address derived from the head live in scalar registers
-  const int h = __builtin_amdgcn_readfirstlane(hg * kWavesPerGroup + (threadIdx.x >> 6));
-  if (h >= a.num_heads) return;
-
   const int L_in = a.context_lens[r];
   const int L = L_in > a.max_context_len ? a.max_context_len : L_in;
   const size_t rh = (size_t)r * a.num_heads + h;
   if (L < 1) {
-    if (split == 0 && (threadIdx.x & 63) < 16) a.out[rh * 16 + (threadIdx.x & 15)] = make_uint4(0u, 0u, 0u, 0u);
+    if (split == 0 && threadIdx.x < 16) a.out[rh * 16 + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
-  if (split >= decode_splits(L)) return;
+  const int nsplit = decode_splits(L);
+  if (split >= nsplit) return;
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const int b0 = split * kSplitBlocks;
+  const int b1 = min(nb, b0 + kSplitBlocks);
   const size_t slot = rh * a.max_splits + split;
   // A row longer than max_context_len is read clamped, for memory safety, but
   // its new token's slot lies past the clamp: it appends nothing.
-  if (kAppend && L_in == L)
-    decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
-                 a.block_tables + (size_t)r * a.bt_stride, L, split, a.q + rh * 16, a.qk_scale, a.out + rh * 16,
-                 a.part_o + slot * kHeadDim, a.part_ml + slot, a.k_new + rh * 16, a.v_new + rh * 16);
-  else
-    decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
-                 a.block_tables + (size_t)r * a.bt_stride, L, split, a.q + rh * 16, a.qk_scale, a.out + rh * 16,
-                 a.part_o + slot * kHeadDim, a.part_ml + slot);
+  const bool app = kAppend && L_in == L;
+  decode_range_waves(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
+                     a.block_tables + (size_t)r * a.bt_stride, L, b0, b1, nsplit == 1, a.q + rh * 16, a.qk_scale,
+                     app ? a.k_new + rh * 16 : nullptr, app ? a.v_new + rh * 16 : nullptr,
+                     reinterpret_cast<uint32_t*>(a.out) + rh * 64, a.part_o + slot * kHeadDim, a.part_ml + slot,
+                     lds);
 }
 
 // Grouped-query decode: G query heads share each KV head.  A workgroup of
@@ -334,13 +329,12 @@ int decode_launch(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, vo
   rs_total = (rs_total + kXcds - 1) / kXcds * kXcds;
 #endif
   if (G == 1) {
-    const int head_groups = (cache->num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
-    const int64_t wgs = rs_total * head_groups;
+    const int64_t wgs = rs_total * cache->num_heads;
     if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
     if (k_new)
-      decode_split_kernel<true><<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
+      decode_kernel<true><<<dim3((unsigned)wgs), dim3(64 * kRangeWaves), 0, s>>>(a);
     else
-      decode_split_kernel<false><<<dim3((unsigned)wgs), dim3(kDecodeThreads), 0, s>>>(a);
+      decode_kernel<false><<<dim3((unsigned)wgs), dim3(64 * kRangeWaves), 0, s>>>(a);
   } else {
     const int64_t wgs = rs_total * cache->num_heads;
     if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");

@@ -1,6 +1,7 @@
-// Decode core shared by the decode launch and the mixed prefill launch: one
-// wave folds one (row, head, range of blocks) of a paged context with an
-// online softmax.  See decode.hip for the mapping onto gfx950.
+// Decode core shared by the decode launch, the mixed prefill launch and the
+// shared-prefix suffix pass: a workgroup folds one (row, head, range of
+// blocks) of a paged context with an online softmax, its waves taking equal
+// shares of the range.  See decode.hip for the mapping onto gfx950.
 #pragma once
 
 #include "device_common.h"
@@ -12,9 +13,6 @@ namespace pkv {
 #ifndef PKV_SPLIT_BLOCKS
 #define PKV_SPLIT_BLOCKS 16
 #endif
-#ifndef PKV_PREFETCH
-#define PKV_PREFETCH 3
-#endif
 // Cache-policy bits of the K/V buffer loads: 2 = nt (streaming).  Keys and
 // values are read once per step, and on gfx950 the non-temporal policy lifts
 // the scattered-slab read rate from ~5.2 to ~6.5 TB/s.
@@ -22,8 +20,19 @@ namespace pkv {
 #define PKV_KV_CPOL 2
 #endif
 
+// Waves that share one range, and the tiles each holds in registers while it
+// folds its share (blocks in flight = depth - 1).
+#ifndef PKV_RANGE_WAVES
+#define PKV_RANGE_WAVES 4
+#endif
+#ifndef PKV_RANGE_DEPTH
+#define PKV_RANGE_DEPTH 3
+#endif
+
 constexpr int kSplitBlocks = PKV_SPLIT_BLOCKS;  // blocks per split-K range
-constexpr int kDepth = PKV_PREFETCH + 1;        // tiles held in registers
+constexpr int kRangeWaves = PKV_RANGE_WAVES;
+constexpr int kRangeDepth = PKV_RANGE_DEPTH;
+static_assert(kSplitBlocks % kRangeWaves == 0, "each wave takes an equal share of a range");
 static_assert(kSplitBlocks >= 1 && kSplitBlocks <= 64, "a range's block ids must fit one wave");
 
 __host__ __device__ constexpr int decode_splits(int L) {
@@ -300,48 +309,185 @@ __device__ __forceinline__ void fold_blocks(const uint16_t* __restrict__ pool, i
   for (int g = 0; g < G; ++g) merge_groups(st[g]);
 }
 
-// Fold range `split` (blocks [split*kSplitBlocks, ...) of a context of L >= 1
-// tokens) for head h on one wave.  With a single range for the row the
-// normalised FP16 output goes to out_head (16 chunks of 8 halves); otherwise
-// the unnormalised partial goes to part_o (128 floats) and (m, l) to
-// *part_ml.
-template <int Depth = kDepth>
-__device__ __forceinline__ void decode_range(const uint16_t* __restrict__ pool, int layer, int num_blocks,
-                                             int num_layers, int num_heads, int h,
-                                             const int32_t* __restrict__ row_table, int L, int split,
-                                             const uint4* __restrict__ q_head, float qk_scale,
-                                             uint4* __restrict__ out_head, float* __restrict__ part_o,
-                                             float2* __restrict__ part_ml, const uint4* __restrict__ new_k = nullptr,
-                                             const uint4* __restrict__ new_v = nullptr) {
+// LDS that the waves of one range combine through (one per workgroup).
+struct RangeScratch {
+  float4 o[kRangeWaves][32];  // each wave's unnormalised output, 128 floats
+  float m[kRangeWaves];
+  float l[kRangeWaves];
+};
+
+// Leave one wave's folded state in lds (lane l < 16 holds dims 8l .. 8l+7).
+__device__ __forceinline__ void store_share(const SoftmaxState& st, RangeScratch& lds, int wave) {
   const int lane = threadIdx.x & 63;
-  const int chunk = lane & 15;
-  const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const int nsplit = (nb + kSplitBlocks - 1) / kSplitBlocks;
-  const int b0 = split * kSplitBlocks;
-  const int b1 = min(nb, b0 + kSplitBlocks);
-  SoftmaxState st;
-  // only the range holding the last token takes the new one
-  const bool last = split == nsplit - 1;
-  fold_blocks<Depth, 1>(pool, layer, num_blocks, num_layers, num_heads, h, row_table, L, b0, b1, q_head, qk_scale, &st,
-                        last ? new_k : nullptr, last ? new_v : nullptr);
-  if (nsplit == 1) {
-    if (lane < 16) {
-      const float inv = 1.0f / st.l;
-      uint4 o;
-      o.x = pack_half2(st.o[0] * inv, st.o[1] * inv);
-      o.y = pack_half2(st.o[2] * inv, st.o[3] * inv);
-      o.z = pack_half2(st.o[4] * inv, st.o[5] * inv);
-      o.w = pack_half2(st.o[6] * inv, st.o[7] * inv);
-      out_head[chunk] = o;
-    }
-  } else {
-    if (lane < 16) {
-      float4* po = reinterpret_cast<float4*>(part_o + chunk * 8);
-      po[0] = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
-      po[1] = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
-    }
-    if (lane == 0) *part_ml = make_float2(st.m, st.l);
+  if (lane < 16) {
+    lds.o[wave][2 * lane] = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+    lds.o[wave][2 * lane + 1] = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
   }
+  if (lane == 0) {
+    lds.m[wave] = st.m;
+    lds.l[wave] = st.l;
+  }
+}
+
+// One wave of a range's workgroup folds its share (see decode_range_waves)
+// and leaves its softmax state in lds.
+__device__ __forceinline__ void fold_range_share(const uint16_t* __restrict__ pool, int layer, int num_blocks,
+                                                 int num_layers, int num_kv_heads, int h_kv,
+                                                 const int32_t* __restrict__ row_table, int L, int b0, int b1,
+                                                 const uint4* __restrict__ q_head, float qk_scale,
+                                                 const uint4* __restrict__ new_k, const uint4* __restrict__ new_v,
+                                                 RangeScratch& lds) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int kPer = kSplitBlocks / kRangeWaves;
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const int w0 = min(b1, b0 + wave * kPer);
+  const int w1 = min(b1, w0 + kPer);
+  const bool takes_new = new_k != nullptr && w0 < w1 && w1 == nb;
+  SoftmaxState st;
+  fold_blocks<kRangeDepth, 1>(pool, layer, num_blocks, num_layers, num_kv_heads, h_kv, row_table, L, w0, w1, q_head,
+                              qk_scale, &st, takes_new ? new_k : nullptr, takes_new ? new_v : nullptr);
+  store_share(st, lds, wave);
+}
+
+// The same shares for nh query heads hq0 .. hq0 + nh - 1 (q_first is head
+// hq0's query, the next heads' follow it), state of head j to lds[j], with no
+// new token.  The tile loads run on across the heads' boundaries, so a wave
+// waits for memory once rather than once per head; each head's blocks fold in
+// the same order with the same arithmetic as in fold_range_share, so its state
+// has the same bits.  q_per_kv query heads share a KV head.
+template <int Depth>
+__device__ __forceinline__ void fold_share_heads(const uint16_t* __restrict__ pool, int layer, int num_blocks,
+                                                 int num_layers, int num_kv_heads, int q_per_kv, int hq0, int nh,
+                                                 const int32_t* __restrict__ row_table, int L, int b0, int b1,
+                                                 const uint4* __restrict__ q_first, float qk_scale,
+                                                 RangeScratch* lds) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int group = lane >> 4;
+  const int chunk = lane & 15;
+  constexpr int kPer = kSplitBlocks / kRangeWaves;
+  const int w0 = min(b1, b0 + wave * kPer);
+  const int n = min(b1, w0 + kPer) - w0;  // blocks in this wave's share
+  SoftmaxState st;
+  auto reset = [&]() {
+    st.m = kMinusBig;
+    st.l = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
+  };
+  reset();
+  if (n <= 0) {
+    // an empty share: the state fold_blocks leaves for no blocks
+    merge_groups(st);
+    for (int j = 0; j < nh; ++j) store_share(st, lds[j], wave);
+    return;
+  }
+  const int my_id = (lane < n) ? row_table[w0 + lane] : 0;
+  const size_t block_stride = (size_t)num_layers * 2 * num_kv_heads * kBlockSize * kHeadDim;
+  const int vdelta = num_kv_heads * kBlockSize * kHeadDim * 2;
+  const int lane_off = group * kHeadDim + chunk * 8;
+  auto head_base = [&](int j) {
+    return pool + slab_offset(0, layer, 0, (hq0 + j) / q_per_kv, num_layers, num_kv_heads);
+  };
+
+  // issue cursor: item (ij, ik) = block w0 + ik of head ij
+  int ij = 0, ik = 0;
+  const uint16_t* ibase = head_base(0);
+  KVTile tile[Depth];
+  bool ok[Depth];
+  auto issue = [&](KVTile& t, bool& good) {
+    const int id = __builtin_amdgcn_readlane(my_id, ik);
+    good = (unsigned)id < (unsigned)num_blocks;
+    load_tile(t, ibase + (size_t)(good ? id : 0) * block_stride, vdelta, lane_off);
+    if (++ik == n) {
+      ik = 0;
+      if (++ij < nh) ibase = head_base(ij);
+    }
+  };
+  const int total = nh * n;
+#pragma unroll
+  for (int u = 0; u < Depth - 1; ++u)
+    if (u < total) issue(tile[u], ok[u]);
+  // the next head's query is loaded a head ahead (clamped to the last head,
+  // so that the load needs no branch)
+  uint4 q = q_first[chunk];
+  uint4 q_next = q_first[min(1, nh - 1) * 16 + chunk];
+  int fj = 0, fk = 0;  // fold cursor
+  for (int i = 0; i < total; i += Depth) {
+#pragma unroll
+    for (int u = 0; u < Depth; ++u) {
+      const int ii = i + u;
+      constexpr int kAhead = Depth - 1;
+      if (ii + kAhead < total) issue(tile[(u + kAhead) % Depth], ok[(u + kAhead) % Depth]);
+      if (ii < total) {
+        const int jj = w0 + fk;
+        const int valid = ok[u] ? min(L - jj * kBlockSize, kBlockSize) : 0;
+        fold_tile<1>(&st, tile[u], &q, qk_scale, group, valid);
+        if (++fk == n) {
+          merge_groups(st);
+          store_share(st, lds[fj], wave);
+          fk = 0;
+          ++fj;
+          reset();
+          q = q_next;
+          q_next = q_first[min(fj + 1, nh - 1) * 16 + chunk];
+        }
+      }
+    }
+  }
+}
+
+// One wave combines the range's shares from lds, in wave order, and writes
+// the result: the normalised FP16 output when the row fits one range
+// (single), otherwise the partial and its (m, l).  Lane l owns dims 2l, 2l+1;
+// a share with no blocks holds m = kMinusBig and l = 0, so it adds nothing.
+__device__ __forceinline__ void combine_range(const RangeScratch& lds, bool single, uint32_t* __restrict__ out_head,
+                                              float* __restrict__ part_o, float2* __restrict__ part_ml) {
+  const int lane = threadIdx.x & 63;
+  float M = kMinusBig;
+#pragma unroll
+  for (int w = 0; w < kRangeWaves; ++w) M = fmaxf(M, lds.m[w]);
+  float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kRangeWaves; ++w) {
+    const float f = fast_exp2(lds.m[w] - M);
+    const float2 v = reinterpret_cast<const float2*>(&lds.o[w][0])[lane];
+    l = fmaf(lds.l[w], f, l);
+    o0 = fmaf(v.x, f, o0);
+    o1 = fmaf(v.y, f, o1);
+  }
+  if (single) {
+    const float inv = 1.0f / l;
+    out_head[lane] = pack_half2(o0 * inv, o1 * inv);
+  } else {
+    reinterpret_cast<float2*>(part_o)[lane] = make_float2(o0, o1);
+    if (lane == 0) *part_ml = make_float2(M, l);
+  }
+}
+
+// Fold the blocks [b0, b1) of one row's range for one query head on a
+// workgroup of kRangeWaves waves.  Wave w folds the w-th equal share of the
+// range (kSplitBlocks / kRangeWaves blocks); the waves' softmax states then
+// combine in wave order (The inference engine, wpnews.pro: the statistics of
+// tiles combine exactly), so the result depends only on the range.  With
+// single (the row fits one range) wave 0 writes the normalised FP16 output to
+// out_head (64 pairs of halves); otherwise the unnormalised partial (128
+// floats) to part_o and (m, l) to *part_ml.  With new_k / new_v, the wave
+// whose share ends at the row's last block takes that token's keys and values
+// and writes them into its slot (the fused append).  Every wave of the
+// workgroup must call this: it synchronises the workgroup.
+__device__ __forceinline__ void decode_range_waves(const uint16_t* __restrict__ pool, int layer, int num_blocks,
+                                                   int num_layers, int num_kv_heads, int h_kv,
+                                                   const int32_t* __restrict__ row_table, int L, int b0, int b1,
+                                                   bool single, const uint4* __restrict__ q_head, float qk_scale,
+                                                   const uint4* __restrict__ new_k, const uint4* __restrict__ new_v,
+                                                   uint32_t* __restrict__ out_head, float* __restrict__ part_o,
+                                                   float2* __restrict__ part_ml, RangeScratch& lds) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  fold_range_share(pool, layer, num_blocks, num_layers, num_kv_heads, h_kv, row_table, L, b0, b1, q_head, qk_scale,
+                   new_k, new_v, lds);
+  __syncthreads();
+  if (wave == 0) combine_range(lds, single, out_head, part_o, part_ml);
 }
 
 // Merge `nsplit` > 1 partials of one (query, head) on one wave: lane s holds

@@ -27,9 +27,10 @@
 // quantization attack different costs").  Key ranges are fixed per row
 // length, so a row's result does not depend on its batch neighbours.
 //
-// Decode rows (n == 1) in the same grid run the decode core (one wave per
-// head and 256-token range).  A merge launch combines the ranges of every
-// query that has more than one.
+// Decode rows (n == 1) in the same grid run the decode core (one workgroup
+// per 256-token range and group of 4 heads, each head's range folded as in
+// the decode launch).  A merge launch combines the ranges of every query that
+// has more than one.
 
 #include <type_traits>
 
@@ -58,7 +59,14 @@ static_assert(kPrefillSplit / kBK <= 64, "a range's block ids for one slot fit o
 constexpr int kRowBytes = kHeadDim * 2;        // one key's 128 dims
 constexpr int kTileBytes = kBK * kRowBytes;     // K (or V) of one step: 16 KiB
 constexpr int kXcds = 8;
+// Tiles a decode wave of the mixed launch holds in registers (blocks in
+// flight = depth - 1).
+#ifndef PKV_MIXED_DEPTH
+#define PKV_MIXED_DEPTH 4
+#endif
 static_assert(kPrefillWaves == 4, "one wave per block of a step");
+static_assert(kPrefillWaves == kRangeWaves, "a decode workgroup of the mixed launch is one range's waves");
+static_assert(kPrefillWaves * sizeof(RangeScratch) <= kTileBytes, "the decode waves combine in one K tile");
 
 // LDS: three K tiles and two V tiles (80 KiB), as distinct objects so that
 // the compiler can tell a tile being filled by direct loads from one being
@@ -525,7 +533,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
     prefill_tile(a, row, qtile, h, kr);
     return;
   }
-  // decode rows: (row, 256-token range, group of kPrefillWaves heads)
+  // decode rows: (row, 256-token range, group of kPrefillWaves query heads)
+  // per workgroup.  Each wave folds its share of the range (as in the decode
+  // launch) for every head of the group in turn, its loads running on from
+  // one head to the next; after one barrier, wave w combines head w.  Each head's arithmetic is the decode launch's, so the
+  // bits are too.  With grouping, the KV head is read once per query head.
   const int head_groups = (a.num_q_heads + kPrefillWaves - 1) / kPrefillWaves;
   const int d = (m - before) * kXcds + x;
   const int hg = d % head_groups;
@@ -533,25 +545,39 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_mixed_kernel(Prefi
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
-  const int h = __builtin_amdgcn_readfirstlane(hg * kPrefillWaves + (threadIdx.x >> 6));
-  if (h >= a.num_q_heads) return;
   const int t = a.query_start[r];
   if (a.query_start[r + 1] - t != 1 || t < 0 || t >= a.total_q) return;
   int L = a.context_lens[r];
   L = L > a.max_context_len ? a.max_context_len : L;
-  const size_t th = (size_t)t * a.num_q_heads + h;
-  if (split == 0 && h == 0 && (threadIdx.x & 63) == 0) a.tok_splits[t] = L < 1 ? 1 : decode_splits(L);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h_own = hg * kPrefillWaves + wave;  // the head this wave combines
+  if (split == 0 && hg == 0 && threadIdx.x == 0) a.tok_splits[t] = L < 1 ? 1 : decode_splits(L);
   if (L < 1) {
-    if (split == 0 && (threadIdx.x & 63) < 16)
-      reinterpret_cast<uint4*>(a.out)[th * 16 + (threadIdx.x & 15)] = make_uint4(0u, 0u, 0u, 0u);
+    if (split == 0 && h_own < a.num_q_heads && (threadIdx.x & 63) < 16)
+      reinterpret_cast<uint4*>(a.out)[((size_t)t * a.num_q_heads + h_own) * 16 + (threadIdx.x & 15)] =
+          make_uint4(0u, 0u, 0u, 0u);
     return;
   }
-  if (split >= decode_splits(L)) return;
+  const int nsplit = decode_splits(L);
+  if (split >= nsplit) return;
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const int b0 = split * kSplitBlocks;
+  const int b1 = min(nb, b0 + kSplitBlocks);
+  // the shares are combined through the first K tile, which a decode workgroup does not use
+  RangeScratch* lds = reinterpret_cast<RangeScratch*>(g_k_tile0);
+  const int32_t* row_table = a.block_tables + (size_t)r * a.bt_stride;
+  const int hq0 = hg * kPrefillWaves;
+  const int nh = min(kPrefillWaves, a.num_q_heads - hq0);
+  fold_share_heads<PKV_MIXED_DEPTH>(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, a.group, hq0, nh,
+                                    row_table, L, b0, b1,
+                                    reinterpret_cast<const uint4*>(a.q) + ((size_t)t * a.num_q_heads + hq0) * 16,
+                                    a.qk_scale, lds);
+  __syncthreads();
+  if (h_own >= a.num_q_heads) return;
+  const size_t th = (size_t)t * a.num_q_heads + h_own;
   const size_t slot = th * a.max_splits + split;
-  // one wave per query head; with grouping, the KV head is read once per query head
-  decode_range(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h / a.group,
-               a.block_tables + (size_t)r * a.bt_stride, L, split, reinterpret_cast<const uint4*>(a.q) + th * 16,
-               a.qk_scale, reinterpret_cast<uint4*>(a.out) + th * 16, a.part_o + slot * kHeadDim, a.part_ml + slot);
+  combine_range(lds[wave], nsplit == 1, reinterpret_cast<uint32_t*>(a.out) + th * 64, a.part_o + slot * kHeadDim,
+                a.part_ml + slot);
 }
 
 // One wave per (query token, head): merge the token's ranges when there is

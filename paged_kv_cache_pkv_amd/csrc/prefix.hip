@@ -36,7 +36,7 @@ constexpr int kPxRowBytes = kHeadDim * 2;             // one key's 128 dims
 constexpr int kPxBlockBytes = kBlockSize * kPxRowBytes;  // 4 KiB: one block of one head, K or V
 constexpr int kPxStepBytes = 2 * kPxBlockBytes;       // a step is two blocks: 32 keys
 constexpr int kPxXcds = 8;
-constexpr int kSuffixWaves = 8;                       // heads per suffix / merge workgroup
+constexpr int kSuffixWaves = 8;                       // heads per merge workgroup
 constexpr int kSuffixThreads = 64 * kSuffixWaves;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -324,22 +324,21 @@ __global__ __launch_bounds__(64) void prefix_tile_kernel(PrefixArgs a) {
 
 // The decode core over every range that is not a prefix range: a sharing
 // row's own ranges from block P on, and the whole context of every other row.
-__global__ __launch_bounds__(kSuffixThreads) void prefix_suffix_kernel(PrefixArgs a) {
-  const int head_groups = (a.num_heads + kSuffixWaves - 1) / kSuffixWaves;
+// One workgroup per (row, range, head), its waves sharing the range as in the
+// decode launch, so an unmarked row gets the decode launch's bits.
+__global__ __launch_bounds__(64 * kRangeWaves) void prefix_suffix_kernel(PrefixArgs a) {
+  __shared__ RangeScratch lds;
   const int n = blockIdx.x;
   const int mq = n / kPxXcds;
-  const int hg = mq % head_groups;
-  const int rs = (n % kPxXcds) + kPxXcds * (mq / head_groups);
+  const int h = mq % a.num_heads;
+  const int rs = (n % kPxXcds) + kPxXcds * (mq / a.num_heads);
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
-  const int h = __builtin_amdgcn_readfirstlane(hg * kSuffixWaves + (threadIdx.x >> 6));
-  if (h >= a.num_heads) return;
-  const int lane = threadIdx.x & 63;
   const int L = clamp_len(a, r);
   const size_t rh = (size_t)r * a.num_heads + h;
   if (L < 1) {
-    if (split == 0 && lane < 16) a.out[rh * 16 + lane] = make_uint4(0u, 0u, 0u, 0u);
+    if (split == 0 && threadIdx.x < 16) a.out[rh * 16 + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
   const bool shared = row_shares(a, L, a.shares[r]);
@@ -354,29 +353,11 @@ __global__ __launch_bounds__(kSuffixThreads) void prefix_suffix_kernel(PrefixArg
   }
   const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int b1 = min(nb, b0 + kSplitBlocks);
-  SoftmaxState st;
-  fold_blocks<kDepth, 1>(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
-                         a.block_tables + (size_t)r * a.bt_stride, L, b0, b1, a.q + rh * 16, a.qk_scale, &st);
-  const int chunk = lane & 15;
-  if (nsplit == 1) {
-    if (lane < 16) {
-      const float inv = 1.0f / st.l;
-      uint4 o;
-      o.x = pack_half2(st.o[0] * inv, st.o[1] * inv);
-      o.y = pack_half2(st.o[2] * inv, st.o[3] * inv);
-      o.z = pack_half2(st.o[4] * inv, st.o[5] * inv);
-      o.w = pack_half2(st.o[6] * inv, st.o[7] * inv);
-      a.out[rh * 16 + chunk] = o;
-    }
-  } else {
-    const size_t slot = rh * a.max_splits + split;
-    if (lane < 16) {
-      float4* po = reinterpret_cast<float4*>(a.part_o + slot * kHeadDim + chunk * 8);
-      po[0] = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
-      po[1] = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
-    }
-    if (lane == 0) a.part_ml[slot] = make_float2(st.m, st.l);
-  }
+  const size_t slot = rh * a.max_splits + split;
+  decode_range_waves(a.pool, a.layer, a.num_blocks, a.num_layers, a.num_heads, h,
+                     a.block_tables + (size_t)r * a.bt_stride, L, b0, b1, nsplit == 1, a.q + rh * 16, a.qk_scale,
+                     nullptr, nullptr, reinterpret_cast<uint32_t*>(a.out) + rh * 64, a.part_o + slot * kHeadDim,
+                     a.part_ml + slot, lds);
 }
 
 __global__ __launch_bounds__(kSuffixThreads) void prefix_merge_kernel(PrefixArgs a) {
@@ -464,11 +445,11 @@ extern "C" int pkv_decode_attention_prefix(const pkv_cache* cache, int32_t layer
     prefix_tile_kernel<<<dim3((unsigned)wgs), dim3(64), 0, st>>>(a);
     if (int rc = check_launch("prefix tile kernel")) return rc;
   }
-  const int head_groups = (cache->num_heads + kSuffixWaves - 1) / kSuffixWaves;
+  const int head_groups = (cache->num_heads + kSuffixWaves - 1) / kSuffixWaves;  // of the merge launch
   const int64_t rs_total = ((int64_t)num_rows * ms + kPxXcds - 1) / kPxXcds * kPxXcds;
-  const int64_t wgs = rs_total * head_groups;
+  const int64_t wgs = rs_total * cache->num_heads;
   if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-  prefix_suffix_kernel<<<dim3((unsigned)wgs), dim3(kSuffixThreads), 0, st>>>(a);
+  prefix_suffix_kernel<<<dim3((unsigned)wgs), dim3(64 * kRangeWaves), 0, st>>>(a);
   if (int rc = check_launch("prefix suffix kernel")) return rc;
   if (ms > 1) {
     prefix_merge_kernel<<<dim3(num_rows, head_groups), dim3(kSuffixThreads), 0, st>>>(a);
