@@ -421,8 +421,10 @@ int pkv_swap_in(const pkv_cache* cache, const void* host_src, const int32_t* ids
  * pkv_append_fp8 takes FP16 k_new / v_new and places them exactly as
  * pkv_append does (same arguments and contract); codes and scales are bit-
  * exact with the definition above.  pkv_decode_attention_fp8 is
- * pkv_decode_attention over the dequantized cache (same arguments, same
- * split-K ranges and workspace size; fp32 arithmetic, FP16 output).
+ * pkv_decode_attention over the dequantized cache (same arguments; split-K
+ * ranges of 512 tokens, which also depend only on the row's own length, and
+ * a workspace of pkv_decode_workspace_size_fp8 bytes; fp32 arithmetic, FP16
+ * output).
  * ---------------------------------------------------------------------- */
 typedef struct pkv_cache8 {
   void* codes;

@@ -15,10 +15,11 @@
 // layer 2 x heads x (128 + 4) bytes are read: 8,448 B at 32 heads instead of
 // 16,384.
 //
-// Decode keeps the FP16 kernel's work split (one wave per (row, head,
-// 256-token range), 4 heads per workgroup, XCD-aware order, the same merge),
-// with one change of lane layout: lane group g holds tokens 4g .. 4g+3 of each
-// block, so its four scales are one 16-byte load.  K codes widen to fp32
+// Decode keeps the FP16 kernel's work split (one workgroup of four waves per
+// (row, head, range), the waves' states combined through LDS, XCD-aware
+// order, the same merge), over 512-token ranges, with one change of lane
+// layout: lane group g holds tokens 4g .. 4g+3 of each block, so its four
+// scales are one 16-byte load.  K codes widen to fp32
 // exactly (v_cvt_pk_f32_fp8); the K scale multiplies the score and the V
 // scale the softmax weight.
 
@@ -30,29 +31,31 @@ namespace {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Two 8-bit blocks in registers per wave (one loading while one folds) keep
-// a wave at 114-122 registers, so four waves fit each SIMD: a CU then holds
+// a wave at 112-118 registers, so four waves fit each SIMD: a CU then holds
 // four 4-wave workgroups, 16 waves with 32 blocks in flight.  Three blocks
-// per wave (three waves per SIMD) measured about 4% slower on the average mix.
+// per wave (three waves per SIMD) measured 2-4% slower on the average mix.
 #ifndef PKV_F8_DEPTH
 #define PKV_F8_DEPTH 2
 #endif
 
 constexpr int kRowCodes = kHeadDim;  // bytes of one (token, head) row
-#ifndef PKV_F8_WAVES
-#define PKV_F8_WAVES 4
-#endif
 #ifndef PKV_F8_SPLIT_BLOCKS
-#define PKV_F8_SPLIT_BLOCKS 16
+#define PKV_F8_SPLIT_BLOCKS 32
 #endif
-constexpr int kF8Waves = PKV_F8_WAVES;  // heads per workgroup, one wave each
-// Blocks per split-K range.  An 8-bit block moves half the bytes of an FP16
-// one, so a range may hold more blocks for the same fixed cost per range.
+// Blocks per split-K range: 512 tokens.  An 8-bit block moves half the bytes
+// of an FP16 one, so a range holds twice the FP16 range's blocks for about the
+// same bytes; each of the range's four waves folds 8 of them.  On the average
+// mix 32 blocks measured 67-71 us per layer against 73-80 at 16 blocks and
+// 77-79 at 64.
 constexpr int kF8SplitBlocks = PKV_F8_SPLIT_BLOCKS;
 static_assert(kF8SplitBlocks >= 1 && kF8SplitBlocks <= 64, "a range's block ids must fit one wave");
+static_assert(kF8SplitBlocks % kRangeWaves == 0, "each wave takes an equal share of a range");
 __host__ __device__ constexpr int f8_splits(int L) {
   return ((L + kBlockSize - 1) / kBlockSize + kF8SplitBlocks - 1) / kF8SplitBlocks;
 }
-constexpr int kF8Threads = 64 * kF8Waves;
+constexpr int kF8DecodeThreads = 64 * kRangeWaves;  // one range's waves
+constexpr int kF8MergeWaves = 4;                     // heads per merge workgroup, one wave each
+constexpr int kF8MergeThreads = 64 * kF8MergeWaves;
 constexpr int kF8Xcds = 8;
 
 struct Cache8 {
@@ -256,18 +259,18 @@ __device__ __forceinline__ void fold_f8(SoftmaxState& st, F8Tile& t, const uint4
   st.m = mn;
 }
 
-// kAppend: the range holding each row's last token quantizes that token from
-// k_new / v_new exactly as pkv_append_fp8 does, folds those codes and scales in
-// place of the slot's stale ones, and writes them into the slot.
+// kAppend: the wave whose share of a range ends at the row's last block
+// quantizes the row's new token from k_new / v_new exactly as pkv_append_fp8
+// does, folds those codes and scales in place of the slot's stale ones, and
+// writes them into the slot.
 template <bool kAppend>
-__global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
-  const int head_groups = (a.c.num_heads + kF8Waves - 1) / kF8Waves;
+__global__ __launch_bounds__(kF8DecodeThreads) void decode_fp8_kernel(F8Args a) {
+  // one workgroup per (row, range, head); heads of a (row, range) back to back on one XCD
+  __shared__ RangeScratch lds;
   const int n = blockIdx.x;
   const int mq = n / kF8Xcds;
-  const int hg = mq % head_groups;
-  const int rs = (n % kF8Xcds) + kF8Xcds * (mq / head_groups);
-  const int h = __builtin_amdgcn_readfirstlane(hg * kF8Waves + (threadIdx.x >> 6));
-  if (h >= a.c.num_heads) return;
+  const int h = mq % a.c.num_heads;
+  const int rs = (n % kF8Xcds) + kF8Xcds * (mq / a.c.num_heads);
   const int split = rs % a.max_splits;
   const int r = rs / a.max_splits;
   if (r >= a.num_rows) return;
@@ -278,14 +281,19 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
   const int chunk = lane & 15;
   const size_t rh = (size_t)r * a.c.num_heads + h;
   if (L < 1) {
-    if (split == 0 && lane < 16) a.out[rh * 16 + lane] = make_uint4(0u, 0u, 0u, 0u);
+    if (split == 0 && threadIdx.x < 16) a.out[rh * 16 + lane] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
   const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int nsplit = f8_splits(L);
   if (split >= nsplit) return;
-  const int b0 = split * kF8SplitBlocks;
-  const int b1 = min(nb, b0 + kF8SplitBlocks);
+  // wave w folds the w-th quarter of the range; the four states combine below
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int kPer = kF8SplitBlocks / kRangeWaves;
+  const int rb0 = split * kF8SplitBlocks;
+  const int rb1 = min(nb, rb0 + kF8SplitBlocks);
+  const int b0 = min(rb1, rb0 + wave * kPer);
+  const int b1 = min(rb1, b0 + kPer);
   const int32_t* row_table = a.block_tables + (size_t)r * a.bt_stride;
   const int my_id = (lane < b1 - b0) ? row_table[b0 + lane] : 0;
   const uint4 q = a.q[rh * 16 + chunk];
@@ -295,9 +303,10 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.o[e] = 0.0f;
 
-  // the new token (slot ns of the last block: group ns / 4, entry ns % 4)
-  // a row clamped to max_context_len appends nothing (its slot lies past the clamp)
-  const bool takes_new = kAppend && split == nsplit - 1 && L_in == L;
+  // the new token (slot ns of the last block: group ns / 4, entry ns % 4),
+  // taken by the wave whose blocks end at the row's last block; a row clamped
+  // to max_context_len appends nothing (its slot lies past the clamp)
+  const bool takes_new = kAppend && b0 < b1 && b1 == nb && L_in == L;
   const int ns = (L - 1) & (kBlockSize - 1);
   u32x2 nkc = u32x2{0u, 0u}, nvc = nkc;
   float nks = 0.0f, nvs = 0.0f;
@@ -357,30 +366,18 @@ __global__ __launch_bounds__(kF8Threads) void decode_fp8_kernel(F8Args a) {
     }
   }
   merge_groups(st);
-  if (nsplit == 1) {
-    if (lane < 16) {
-      const float inv = 1.0f / st.l;
-      uint4 o;
-      o.x = pack_half2(st.o[0] * inv, st.o[1] * inv);
-      o.y = pack_half2(st.o[2] * inv, st.o[3] * inv);
-      o.z = pack_half2(st.o[4] * inv, st.o[5] * inv);
-      o.w = pack_half2(st.o[6] * inv, st.o[7] * inv);
-      a.out[rh * 16 + chunk] = o;
-    }
-  } else {
+  store_share(st, lds, wave);
+  __syncthreads();
+  if (wave == 0) {
     const size_t slot = rh * a.max_splits + split;
-    if (lane < 16) {
-      float4* po = reinterpret_cast<float4*>(a.part_o + slot * kHeadDim + chunk * 8);
-      po[0] = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
-      po[1] = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
-    }
-    if (lane == 0) a.part_ml[slot] = make_float2(st.m, st.l);
+    combine_range(lds, nsplit == 1, reinterpret_cast<uint32_t*>(a.out) + rh * 64, a.part_o + slot * kHeadDim,
+                  a.part_ml + slot);
   }
 }
 
-__global__ __launch_bounds__(kF8Threads) void merge_fp8_kernel(F8Args a) {
+__global__ __launch_bounds__(kF8MergeThreads) void merge_fp8_kernel(F8Args a) {
   const int r = blockIdx.x;
-  const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kF8Waves + (threadIdx.x >> 6));
+  const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * kF8MergeWaves + (threadIdx.x >> 6));
   if (h >= a.c.num_heads) return;
   int L = a.context_lens[r];
   L = L > a.max_context_len ? a.max_context_len : L;
@@ -491,17 +488,17 @@ int decode_fp8_launch(const pkv_cache8* cache, int32_t layer, void* out, const v
   a.max_splits = ms;
   a.qk_scale = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int head_groups = (cache->num_heads + kF8Waves - 1) / kF8Waves;
+  const int head_groups = (cache->num_heads + kF8MergeWaves - 1) / kF8MergeWaves;
   int64_t rs_total = ((int64_t)num_rows * ms + kF8Xcds - 1) / kF8Xcds * kF8Xcds;
-  const int64_t wgs = rs_total * head_groups;
+  const int64_t wgs = rs_total * cache->num_heads;
   if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
   if (k_new)
-    decode_fp8_kernel<true><<<dim3((unsigned)wgs), dim3(kF8Threads), 0, s>>>(a);
+    decode_fp8_kernel<true><<<dim3((unsigned)wgs), dim3(kF8DecodeThreads), 0, s>>>(a);
   else
-    decode_fp8_kernel<false><<<dim3((unsigned)wgs), dim3(kF8Threads), 0, s>>>(a);
+    decode_fp8_kernel<false><<<dim3((unsigned)wgs), dim3(kF8DecodeThreads), 0, s>>>(a);
   if (int rc = check_launch("decode fp8 kernel")) return rc;
   if (ms > 1) {
-    merge_fp8_kernel<<<dim3(num_rows, head_groups), dim3(kF8Threads), 0, s>>>(a);
+    merge_fp8_kernel<<<dim3(num_rows, head_groups), dim3(kF8MergeThreads), 0, s>>>(a);
     if (int rc = check_launch("merge fp8 kernel")) return rc;
   }
   return PKV_OK;

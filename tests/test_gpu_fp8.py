@@ -58,6 +58,8 @@ def test_append_fp8_bitexact(which):
 CASES = [
     # name, heads, layers, lens
     ("ragged", 32, 1, [1, 2, 15, 16, 17, 100, 255, 256, 257, 512]),
+    # the edges of a wave's 128-token share and of a 512-token range
+    ("share-edges", 8, 1, [127, 128, 129, 383, 384, 385, 511, 512, 513, 1024, 1025]),
     ("multi-split", 32, 2, [513, 1025, 2600]),
     ("odd-heads", 5, 1, [300, 1, 700]),
     # the most heads the library accepts
@@ -92,9 +94,9 @@ def test_decode_fp8_parity(name, heads, layers, lens):
 
 
 def test_decode_fp8_beyond_64_ranges():
-    """Rows of 79 and 65 ranges: the 8-bit merge takes its ranges in several passes of 64."""
+    """Rows of 79 and 66 ranges of 512 tokens: the 8-bit merge takes its ranges in several passes of 64."""
     torch = torch_cuda()
-    lens = [20000, 16400, 300]
+    lens = [40000, 33300, 300]
     b = build_batch("fp8-long", 33, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 4,
                     num_layers=1, num_heads=2, stride=max(-(-L // 16) for L in lens))
     pool = opaged.append(b.pool, 0, b.k_new[0], b.v_new[0], b.positions, b.request_of_token, b.block_tables)
