@@ -309,15 +309,18 @@ __device__ __forceinline__ void fold_blocks(const uint16_t* __restrict__ pool, i
   for (int g = 0; g < G; ++g) merge_groups(st[g]);
 }
 
-// LDS that the waves of one range combine through (one per workgroup).
-struct RangeScratch {
-  float4 o[kRangeWaves][32];  // each wave's unnormalised output, 128 floats
-  float m[kRangeWaves];
-  float l[kRangeWaves];
+// LDS that the W waves of one range combine through (one per workgroup).
+template <int W>
+struct RangeScratchW {
+  float4 o[W][32];  // each wave's unnormalised output, 128 floats
+  float m[W];
+  float l[W];
 };
+using RangeScratch = RangeScratchW<kRangeWaves>;
 
 // Leave one wave's folded state in lds (lane l < 16 holds dims 8l .. 8l+7).
-__device__ __forceinline__ void store_share(const SoftmaxState& st, RangeScratch& lds, int wave) {
+template <int W>
+__device__ __forceinline__ void store_share(const SoftmaxState& st, RangeScratchW<W>& lds, int wave) {
   const int lane = threadIdx.x & 63;
   if (lane < 16) {
     lds.o[wave][2 * lane] = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
@@ -441,15 +444,17 @@ __device__ __forceinline__ void fold_share_heads(const uint16_t* __restrict__ po
 // the result: the normalised FP16 output when the row fits one range
 // (single), otherwise the partial and its (m, l).  Lane l owns dims 2l, 2l+1;
 // a share with no blocks holds m = kMinusBig and l = 0, so it adds nothing.
-__device__ __forceinline__ void combine_range(const RangeScratch& lds, bool single, uint32_t* __restrict__ out_head,
-                                              float* __restrict__ part_o, float2* __restrict__ part_ml) {
+template <int W>
+__device__ __forceinline__ void combine_range(const RangeScratchW<W>& lds, bool single,
+                                              uint32_t* __restrict__ out_head, float* __restrict__ part_o,
+                                              float2* __restrict__ part_ml) {
   const int lane = threadIdx.x & 63;
   float M = kMinusBig;
 #pragma unroll
-  for (int w = 0; w < kRangeWaves; ++w) M = fmaxf(M, lds.m[w]);
+  for (int w = 0; w < W; ++w) M = fmaxf(M, lds.m[w]);
   float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kRangeWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     const float f = fast_exp2(lds.m[w] - M);
     const float2 v = reinterpret_cast<const float2*>(&lds.o[w][0])[lane];
     l = fmaf(lds.l[w], f, l);

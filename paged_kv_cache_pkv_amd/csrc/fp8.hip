@@ -49,11 +49,15 @@ constexpr int kRowCodes = kHeadDim;  // bytes of one (token, head) row
 // 77-79 at 64.
 constexpr int kF8SplitBlocks = PKV_F8_SPLIT_BLOCKS;
 static_assert(kF8SplitBlocks >= 1 && kF8SplitBlocks <= 64, "a range's block ids must fit one wave");
-static_assert(kF8SplitBlocks % kRangeWaves == 0, "each wave takes an equal share of a range");
+#ifndef PKV_F8_RANGE_WAVES
+#define PKV_F8_RANGE_WAVES 4
+#endif
+constexpr int kF8RangeWaves = PKV_F8_RANGE_WAVES;  // waves that share one range
+static_assert(kF8SplitBlocks % kF8RangeWaves == 0, "each wave takes an equal share of a range");
 __host__ __device__ constexpr int f8_splits(int L) {
   return ((L + kBlockSize - 1) / kBlockSize + kF8SplitBlocks - 1) / kF8SplitBlocks;
 }
-constexpr int kF8DecodeThreads = 64 * kRangeWaves;  // one range's waves
+constexpr int kF8DecodeThreads = 64 * kF8RangeWaves;  // one range's waves
 constexpr int kF8MergeWaves = 4;                     // heads per merge workgroup, one wave each
 constexpr int kF8MergeThreads = 64 * kF8MergeWaves;
 constexpr int kF8Xcds = 8;
@@ -266,7 +270,7 @@ __device__ __forceinline__ void fold_f8(SoftmaxState& st, F8Tile& t, const uint4
 template <bool kAppend>
 __global__ __launch_bounds__(kF8DecodeThreads) void decode_fp8_kernel(F8Args a) {
   // one workgroup per (row, range, head); heads of a (row, range) back to back on one XCD
-  __shared__ RangeScratch lds;
+  __shared__ RangeScratchW<kF8RangeWaves> lds;
   const int n = blockIdx.x;
   const int mq = n / kF8Xcds;
   const int h = mq % a.c.num_heads;
@@ -287,9 +291,9 @@ __global__ __launch_bounds__(kF8DecodeThreads) void decode_fp8_kernel(F8Args a) 
   const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int nsplit = f8_splits(L);
   if (split >= nsplit) return;
-  // wave w folds the w-th quarter of the range; the four states combine below
+  // wave w folds the w-th equal share of the range; the states combine below
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int kPer = kF8SplitBlocks / kRangeWaves;
+  constexpr int kPer = kF8SplitBlocks / kF8RangeWaves;
   const int rb0 = split * kF8SplitBlocks;
   const int rb1 = min(nb, rb0 + kF8SplitBlocks);
   const int b0 = min(rb1, rb0 + wave * kPer);
