@@ -41,6 +41,7 @@ namespace {
 constexpr int kWavesPerGroup = 4;  // heads per merge workgroup
 constexpr int kDecodeThreads = 64 * kWavesPerGroup;
 constexpr int kXcds = 8;
+constexpr int kRowBytesGqm = kHeadDim * 2;  // one token row of one head
 
 struct DecodeArgs {
   const uint16_t* pool;
@@ -217,6 +218,273 @@ __global__ __launch_bounds__(64 * gqa_waves<G>()) void decode_gqa_kernel(DecodeA
   }
 }
 
+// Grouped-query decode on the matrix cores.  With G query heads per KV head
+// the per-block work of a wave is two small matrix products, and on the
+// vector ALUs it grows with G (the scores' lane reductions and P*V).  Here a
+// 16-token block of one KV head folds into up to 16 query slots (G used, the
+// rest zero) as:
+//   S = K Q^T       v_mfma_f32_16x16x32_f16 x 4 (128 dims): A = the block's
+//                   K rows, loaded from memory straight into the A layout
+//                   (lane (g, t) holds dims 32c + 8g .. +7 of token t), B =
+//                   the queries, held in registers for the whole range;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_f16 x 8 (16 dims each): B = P^T,
+//                   which is S's accumulator rounded to FP16 (lane (g, q)
+//                   holds tokens 4g .. 4g+3 of query slot q), A = V^T, read
+//                   from the block's V rows in LDS by ds_read_tr16_b64 (a
+//                   16-lane group reads 4 rows x 16 dims and hands lane i the
+//                   4 rows of dim i).
+// V reaches LDS by direct global->LDS loads (no registers), K by ordinary
+// loads into registers; each wave holds kGqmDepth blocks in its own LDS
+// tiles and registers, one loading while one folds.  At two blocks the
+// kernel fits 168 registers, three waves per SIMD; on the average mix with 8
+// KV heads it takes 31 us per layer at G = 8 against 37 us for the vector
+// fold, and ties it at G = 4 (45 us); at G = 2 the vector fold is faster
+// (68 against 90 us), since 14 of the 16 query slots would be idle.  The
+// online softmax is the grouped fold's: a lazy exponent reference
+// (kGroupLazy) and FP16 weights whose rounded values also form the row sum.  Lane (g, q) keeps query slot q's statistics; the maximum over a
+// block's 16 tokens is one exchange across the four lane groups.  Rows past
+// the context read as zero through the buffer resource's range and get score
+// -inf.  The range partition and the combine of the waves through LDS are
+// the vector kernel's.
+#ifndef PKV_GQM_WAVES
+#define PKV_GQM_WAVES 4
+#endif
+#ifndef PKV_GQM_DEPTH
+#define PKV_GQM_DEPTH 2
+#endif
+// group sizes from which the matrix-core kernel replaces the vector one
+// (G = 4 and 8; G = 2 stays on the vector fold)
+#ifndef PKV_GQA_MFMA_MIN_G
+#define PKV_GQA_MFMA_MIN_G 4
+#endif
+constexpr int kGqmWaves = PKV_GQM_WAVES;
+constexpr int kGqmDepth = PKV_GQM_DEPTH;
+constexpr int kVTileBytes = kBlockSize * kHeadDim * 2;  // one block's V rows of one head
+static_assert(kSplitBlocks % kGqmWaves == 0, "each wave takes an equal share of a range");
+static_assert(kGqmDepth >= 2 && kGqmDepth <= 4, "blocks in flight per wave");
+
+typedef short gqm_v4i16 __attribute__((ext_vector_type(4)));
+#define PKV_GQM_LDS __attribute__((address_space(3)))
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (they complete in issue order), and keep memory accesses from
+// moving across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(N == 8 || N == 16 || N == 24, "eight operations per block");
+  if constexpr (N == 8)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 16)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+}
+
+#ifndef PKV_GQM_OCC
+#define PKV_GQM_OCC 1
+#endif
+template <int G, bool kAppend>
+__global__ __launch_bounds__(64 * kGqmWaves, PKV_GQM_OCC) void decode_gqa_mfma_kernel(DecodeArgs a) {
+  static_assert(G >= 2 && G <= 16, "the query slots of one 16-column product");
+  constexpr int D = kGqmDepth;
+  constexpr int kPer = kSplitBlocks / kGqmWaves;
+  __shared__ __attribute__((aligned(16))) char s_tiles[kGqmWaves * D * kVTileBytes];
+  __shared__ float s_m[kGqmWaves][G], s_l[kGqmWaves][G];
+  static_assert(sizeof(float4) * kGqmWaves * G * 32 <= sizeof(s_tiles), "the combine reuses the V tiles");
+  float4(*s_o)[G][32] = reinterpret_cast<float4(*)[G][32]>(s_tiles);
+  const int n = blockIdx.x;
+#if PKV_XCD_REMAP
+  const int mx = n / kXcds;
+  const int h = mx % a.num_heads;
+  const int rs = (n % kXcds) + kXcds * (mx / a.num_heads);
+#else
+  const int h = n % a.num_heads;
+  const int rs = n / a.num_heads;
+#endif
+  const int split = rs % a.max_splits;
+  const int r = rs / a.max_splits;
+  if (r >= a.num_rows) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int gg = lane >> 4;   // lane group: tokens 4gg .. 4gg+3 of S, dims 32c + 8gg of K
+  const int col = lane & 15;  // token of K's A operand; query slot of S, P and O^T
+  const int L_in = a.context_lens[r];
+  const int L = L_in > a.max_context_len ? a.max_context_len : L_in;
+  const size_t rh = (size_t)r * a.num_q_heads + (size_t)h * G;  // the KV head's first query head
+  if (L < 1) {
+    if (split == 0 && wave == 0 && lane < 16)
+#pragma unroll
+      for (int g = 0; g < G; ++g) a.out[(rh + g) * 16 + lane] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  const int nsplit = decode_splits(L);
+  if (split >= nsplit) return;
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const int b0 = min(nb, split * kSplitBlocks + wave * kPer);
+  const int b1 = min(nb, b0 + kPer);
+
+  // B operand of S = K Q^T: dims 32c + 8gg .. +7 of query slot col
+  half8_t qb[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qb[c] = col < G ? bitcast<half8_t>(a.q[(rh + col) * 16 + 4 * c + gg]) : half8_t{};
+
+  const uint16_t* head_base = a.pool + slab_offset(0, a.layer, 0, h, a.num_layers, a.num_heads);
+  const size_t block_stride = (size_t)a.num_layers * 2 * a.num_heads * kBlockSize * kHeadDim;
+  const int vdelta = a.num_heads * kBlockSize * kHeadDim * 2;  // bytes from a head's K tile to its V tile
+  const int32_t* row_table = a.block_tables + (size_t)r * a.bt_stride;
+  const int my_id = (lane < b1 - b0) ? row_table[b0 + lane] : 0;
+  // the V rows sit in LDS with chunk k of row t at chunk position k ^ (t & 15)
+  int v_src[4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    const int row = 4 * qd + gg;
+    v_src[qd] = vdelta + row * kRowBytesGqm + ((col ^ (row & 15)) << 4);
+  }
+  const int tr_row = 4 * gg + (col >> 2);
+  int tr_off[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int dim = 16 * c + 4 * (col & 3);
+    tr_off[c] = tr_row * kRowBytesGqm + (((dim >> 3) ^ (tr_row & 15)) << 4) + (dim & 7) * 2;
+  }
+  char* my_tiles = s_tiles + wave * D * kVTileBytes;
+
+  // Issue block j's loads into slot `slot`: 4 K loads into registers, then 4
+  // direct V loads into the slot's LDS tile.  Slots past the share issue the
+  // same 8 operations on an empty range, so that every block is followed by
+  // exactly D - 1 blocks' operations.
+  half8_t kr[D][4];
+  int rows_of[D];
+  auto issue = [&](int slot, int j) {
+    const bool live = j < b1;
+    const int id = __builtin_amdgcn_readlane(my_id, live ? j - b0 : 0);
+    const bool good = live && (unsigned)id < (unsigned)a.num_blocks;
+    const int rows = good ? min(L - j * kBlockSize, kBlockSize) : 0;
+    const uint16_t* base = head_base + (size_t)(good ? id : 0) * block_stride;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base), 0, good ? vdelta + rows * kRowBytesGqm : 0, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      kr[slot][c] = bitcast<half8_t>(
+          __builtin_amdgcn_raw_buffer_load_b128(rsrc, col * kRowBytesGqm + 64 * c + 16 * gg, 0, PKV_KV_CPOL));
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (PKV_GQM_LDS void*)(my_tiles + slot * kVTileBytes + qd * 1024), 16,
+                                               v_src[qd], 0, 0, PKV_KV_CPOL);
+    rows_of[slot] = rows;
+  };
+
+  // with the append fused, the wave whose share ends at the row's last block takes the new token
+  bool takes_new = false;
+  if constexpr (kAppend) takes_new = b0 < b1 && b1 == nb && L_in == L;
+  const int s_new = (L - 1) & (kBlockSize - 1);
+
+  float4_t o[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = kMinusBig, l = 0.0f;
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u) issue(u, b0 + u);
+  for (int j = b0; j < b1; j += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int jj = j + u;
+      if (jj < b1) {
+        issue((u + D - 1) % D, jj + D - 1);
+        wait_vmem_at_most<8 * (D - 1)>();  // block jj's K registers and V tile have landed
+        char* tile = my_tiles + u * kVTileBytes;
+        const int valid = rows_of[u];
+        if (kAppend && takes_new && jj == nb - 1 && valid > 0) {
+          const uint4* new_k = a.k_new + ((size_t)r * a.num_heads + h) * 16;
+          const uint4* new_v = a.v_new + ((size_t)r * a.num_heads + h) * 16;
+          if (col == s_new)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kr[u][c] = bitcast<half8_t>(new_k[4 * c + gg]);
+          if (lane < 16) {
+            const uint4 nk = new_k[lane], nv = new_v[lane];
+            *reinterpret_cast<uint4*>(tile + s_new * kRowBytesGqm + ((lane ^ (s_new & 15)) << 4)) = nv;
+            const int id = __builtin_amdgcn_readlane(my_id, jj - b0);
+            uint16_t* slot_k = const_cast<uint16_t*>(head_base) + (size_t)id * block_stride + s_new * kHeadDim + lane * 8;
+            *reinterpret_cast<uint4*>(slot_k) = nk;
+            *reinterpret_cast<uint4*>(reinterpret_cast<char*>(slot_k) + vdelta) = nv;
+          }
+        }
+        float4_t sc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[u][c], qb[c], sc, 0, 0, 0);
+        if (valid < kBlockSize) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * gg + i >= valid) sc[i] = -INFINITY;
+        }
+        float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.qk_scale;
+        mb = fmaxf(mb, shfl_xor(mb, 16));
+        mb = fmaxf(mb, shfl_xor(mb, 32));
+        if (__any(mb > m + kGroupLazy)) {
+          const float mn = fmaxf(m, mb);
+          const float alpha = fast_exp2(m - mn);
+          l *= alpha;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[c] *= alpha;
+          m = mn;
+        }
+        half4_t pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = (_Float16)fast_exp2(fmaf(sc[i], a.qk_scale, -m));
+        l = __builtin_amdgcn_fdot2(half2_t{pb[2], pb[3]}, ones,
+                                   __builtin_amdgcn_fdot2(half2_t{pb[0], pb[1]}, ones, l, false), false);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const gqm_v4i16 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_GQM_LDS gqm_v4i16*)(tile + tr_off[c]));
+          o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<half4_t>(vt), pb, o[c], 0, 0, 0);
+        }
+      }
+    }
+  }
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  // every direct load of this wave (the trailing empty ones too) has landed
+  // and every LDS read has returned before the tiles become the combine's
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (col < G) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s_o[wave][col][4 * c + gg] = make_float4(o[c][0], o[c][1], o[c][2], o[c][3]);
+    if (gg == 0) {
+      s_m[wave][col] = m;
+      s_l[wave][col] = l;
+    }
+  }
+  __syncthreads();
+  // wave w combines query heads g = w, w + kGqmWaves, ...; lane owns dims 2*lane, 2*lane + 1
+  for (int g = wave; g < G; g += kGqmWaves) {
+    float M = kMinusBig;
+#pragma unroll
+    for (int w = 0; w < kGqmWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float lt = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGqmWaves; ++w) {
+      const float f = fast_exp2(s_m[w][g] - M);
+      const float2 v = reinterpret_cast<const float2*>(&s_o[w][g][0])[lane];
+      lt = fmaf(s_l[w][g], f, lt);
+      o0 = fmaf(v.x, f, o0);
+      o1 = fmaf(v.y, f, o1);
+    }
+    const size_t hq = rh + g;
+    if (nsplit == 1) {
+      const float inv = 1.0f / lt;
+      reinterpret_cast<uint32_t*>(a.out)[hq * 64 + lane] = pack_half2(o0 * inv, o1 * inv);
+    } else {
+      const size_t slot = hq * a.max_splits + split;
+      reinterpret_cast<float2*>(a.part_o + slot * kHeadDim)[lane] = make_float2(o0, o1);
+      if (lane == 0) a.part_ml[slot] = make_float2(M, lt);
+    }
+  }
+}
+
 // Merge the ranges of every (row, head) that has more than one; one wave per
 // (row, head).
 __global__ __launch_bounds__(kDecodeThreads) void decode_merge_kernel(DecodeArgs a) {
@@ -339,17 +607,34 @@ int decode_launch(const pkv_cache* cache, int32_t num_q_heads, int32_t layer, vo
     const int64_t wgs = rs_total * cache->num_heads;
     if (wgs > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
     const dim3 grid((unsigned)wgs);
+    const dim3 mfma_block(64 * kGqmWaves);
     if (k_new) {
-      switch (G) {
-        case 2: decode_gqa_kernel<2, true><<<grid, dim3(64 * gqa_waves<2>()), 0, s>>>(a); break;
-        case 4: decode_gqa_kernel<4, true><<<grid, dim3(64 * gqa_waves<4>()), 0, s>>>(a); break;
-        default: decode_gqa_kernel<8, true><<<grid, dim3(64 * gqa_waves<8>()), 0, s>>>(a); break;
+      if (G >= PKV_GQA_MFMA_MIN_G) {
+        switch (G) {
+          case 2: decode_gqa_mfma_kernel<2, true><<<grid, mfma_block, 0, s>>>(a); break;
+          case 4: decode_gqa_mfma_kernel<4, true><<<grid, mfma_block, 0, s>>>(a); break;
+          default: decode_gqa_mfma_kernel<8, true><<<grid, mfma_block, 0, s>>>(a); break;
+        }
+      } else {
+        switch (G) {
+          case 2: decode_gqa_kernel<2, true><<<grid, dim3(64 * gqa_waves<2>()), 0, s>>>(a); break;
+          case 4: decode_gqa_kernel<4, true><<<grid, dim3(64 * gqa_waves<4>()), 0, s>>>(a); break;
+          default: decode_gqa_kernel<8, true><<<grid, dim3(64 * gqa_waves<8>()), 0, s>>>(a); break;
+        }
       }
     } else {
-      switch (G) {
-        case 2: decode_gqa_kernel<2, false><<<grid, dim3(64 * gqa_waves<2>()), 0, s>>>(a); break;
-        case 4: decode_gqa_kernel<4, false><<<grid, dim3(64 * gqa_waves<4>()), 0, s>>>(a); break;
-        default: decode_gqa_kernel<8, false><<<grid, dim3(64 * gqa_waves<8>()), 0, s>>>(a); break;
+      if (G >= PKV_GQA_MFMA_MIN_G) {
+        switch (G) {
+          case 2: decode_gqa_mfma_kernel<2, false><<<grid, mfma_block, 0, s>>>(a); break;
+          case 4: decode_gqa_mfma_kernel<4, false><<<grid, mfma_block, 0, s>>>(a); break;
+          default: decode_gqa_mfma_kernel<8, false><<<grid, mfma_block, 0, s>>>(a); break;
+        }
+      } else {
+        switch (G) {
+          case 2: decode_gqa_kernel<2, false><<<grid, dim3(64 * gqa_waves<2>()), 0, s>>>(a); break;
+          case 4: decode_gqa_kernel<4, false><<<grid, dim3(64 * gqa_waves<4>()), 0, s>>>(a); break;
+          default: decode_gqa_kernel<8, false><<<grid, dim3(64 * gqa_waves<8>()), 0, s>>>(a); break;
+        }
       }
     }
   }
