@@ -52,9 +52,11 @@ def test_gqa_decode_parity(G):
     torch = torch_cuda()
     Hkv = 8 if G < 8 else 4
     Hq = Hkv * G
-    lens = [1, 15, 16, 17, 255, 256, 257, 700, 2600]
-    b = build_batch(f"gqa-decode-G{G}", 40 + G, lens, [1] * len(lens), num_blocks=300, num_layers=2,
-                    num_heads=Hkv, stride=170)
+    # lengths at the edges of a block, of a wave's share of a range (64 tokens
+    # on the matrix-core fold, 128 on the vector one) and of a range
+    lens = [1, 15, 16, 17, 63, 64, 65, 127, 129, 191, 193, 255, 256, 257, 700, 2600]
+    b = build_batch(f"gqa-decode-G{G}", 40 + G, lens, [1] * len(lens), num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                    num_layers=2, num_heads=Hkv, stride=170)
     q = _queries(50 + G, len(lens), Hq)
     pool = _full_pool(b)
     say(f"gqa decode G={G} Hkv={Hkv}")
