@@ -572,12 +572,13 @@ def measure_long_context(torch, pkv, cache, stream, steps=5, warm=2):
     }
 
 
-def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, warm=3, payload=None):
+def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, warm=3, payload=None, counted=True):
     """Grouped-query decode: the average mix's tables and lengths over a
-    32-layer pool of 8 KV heads (2 MiB blocks), 32 query heads (groups of 4);
-    per layer one decode launch.  Bytes = K and V of 8 heads per token.  With
-    `payload` (a list), layer 0's first output and the blocks it read are
-    kept for the oracle leg."""
+    32-layer pool of kv_heads KV heads, q_heads query heads (8 and 32: groups
+    of 4; 4 and 32: groups of 8); per layer one decode launch.  Bytes = K and
+    V of the KV heads per token.  With `payload` (a list), layer 0's first
+    output and the blocks it read are kept for the oracle leg.  `counted`:
+    the committed counter summary covers this shape (groups of 4)."""
     from workloads import SCALE, fill_normal_fp16_device
 
     NB, NL = 7152, 32
@@ -644,7 +645,7 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
         "kv_tokens_per_s": tokens / (ms / 1e3),
         "hbm_tb_s": kv_bytes / (ms / 1e3) / 1e12,
         "hbm_frac_of_peak": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-        "traffic_bytes_per_launch": fp8_gqa_traffic("gqa"),
+        "traffic_bytes_per_launch": fp8_gqa_traffic("gqa") if counted else None,
     }
 
 
@@ -846,8 +847,8 @@ def oracle_cpu_baseline(args, sample, tables, lens, q_bits, gpu_outs, layer_name
 
 
 def gqa_parity(payload):
-    """The grouped-query leg's first decode (layer 0, G = 4, weights rounded to
-    FP16 before P.V) against the fp64 oracle."""
+    """A grouped-query leg's first decode (layer 0, G = 4 or 8, weights
+    rounded to FP16 before P.V) against the fp64 oracle."""
     import oracle.paged as opaged
     from tests.tolerance import compare
     from workloads import SCALE
@@ -1024,8 +1025,9 @@ def main():
     achieved = bytes_per_decode / (dec_avg_ms / 1e3) / 1e9
     traffic = counted_traffic()
 
-    blocks = long_ctx = gqa = fp8 = tiny = probe = None
+    blocks = long_ctx = gqa = gqa8 = fp8 = tiny = probe = None
     gqa_payload = [] if cpu_sample is not None else None
+    gqa8_payload = [] if cpu_sample is not None else None
     if not args.no_extra:
         probe = measure_bandwidth(torch, pkv, cache, tables, tlen, stream)
         blocks = measure_block_copies(torch, pkv, cache, bp.free_list(), stream)
@@ -1033,6 +1035,7 @@ def main():
         del pool_d, cache
         torch.cuda.empty_cache()
         gqa = measure_gqa(torch, pkv, batch, stream, payload=gqa_payload)
+        gqa8 = measure_gqa(torch, pkv, batch, stream, kv_heads=4, q_heads=32, payload=gqa8_payload, counted=False)
         fp8 = measure_fp8(torch, pkv, batch, stream)
         tiny = measure_tiny(torch, pkv, dev, stream)
     else:
@@ -1065,6 +1068,8 @@ def main():
                                                    q_bits, step0_outs, list(ORACLE_LAYERS))
         if gqa is not None and gqa_payload:
             gqa["parity"] = gqa_parity(gqa_payload[0])
+        if gqa8 is not None and gqa8_payload:
+            gqa8["parity"] = gqa_parity(gqa8_payload[0])
         if trace is not None and checkers:
             for name, chk in checkers:
                 tot = chk.check(rows=TRACE_CHECK_ROWS)
@@ -1111,6 +1116,7 @@ def main():
         "trace": trace,
         "long_context": long_ctx,
         "gqa_decode": gqa,
+        "gqa8_decode": gqa8,
         "fp8_decode": fp8,
         "block_copy": blocks,
         "tiny_decode": tiny,
@@ -1120,7 +1126,8 @@ def main():
         ceiling = probe["slab_read_gb_s"] / 1e3  # TB/s
         rec["roofline"]["frac_of_achievable"] = achieved / probe["slab_read_gb_s"]
         # the grouped-query, 8-bit and long-context decodes against the same measured read ceiling
-        for leg, key in (("gqa_decode", "hbm_tb_s"), ("fp8_decode", "hbm_tb_s"), ("long_context", "hbm_tb_s")):
+        for leg, key in (("gqa_decode", "hbm_tb_s"), ("gqa8_decode", "hbm_tb_s"), ("fp8_decode", "hbm_tb_s"),
+                         ("long_context", "hbm_tb_s")):
             if rec.get(leg) and rec[leg].get(key):
                 rec[leg]["frac_of_achievable"] = rec[leg][key] / ceiling
                 rec[leg]["achievable_note"] = "the FP16 average-mix slab probe (256 KiB slabs) as the read ceiling"

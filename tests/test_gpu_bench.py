@@ -30,7 +30,7 @@ def test_bench_runs_every_leg():
     assert rec["n_gpus"] == 1 and rec["value"] > 0 and rec["config"]["workload"]
     roof = rec["roofline"]
     assert roof["bound"] == "hbm" and 0 < roof["frac"] < 1 and roof["achievable"]["slab_read_gb_s"] > 0
-    for leg in ("prefill", "trace", "long_context", "gqa_decode", "fp8_decode", "block_copy", "tiny_decode"):
+    for leg in ("prefill", "trace", "long_context", "gqa_decode", "gqa8_decode", "fp8_decode", "block_copy", "tiny_decode"):
         assert rec[leg], leg
     assert 0 < rec["prefill"]["roofline"]["frac"] < 1
     assert 0 < rec["prefill"]["roofline"]["frac_of_achievable"] < 1
