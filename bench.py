@@ -237,7 +237,7 @@ def _run_trace(torch, steps, warm, shared_decode, cold_steps=20, checker=False):
             if i in TRACE_SAMPLED:
                 chk.keep(snap)
         sharers = sum(1 for r in tr.rows if r.shared)
-        rec.append((ev, int(snap["lens"].sum()), sharers, snap["host_ms"]))
+        rec.append((ev, int(snap["lens"].sum()), sharers, snap["host_ms"], snap["stage_wait_ms"]))
     torch.cuda.synchronize()
     # cold: the 256 MB last-level cache scrubbed (a 512 MB write, not timed)
     # before each step's decode part
@@ -252,19 +252,20 @@ def _run_trace(torch, steps, warm, shared_decode, cold_steps=20, checker=False):
     torch.cuda.synchronize()
     del scrub
     cold_ms = np.array([e[2].elapsed_time(e[3]) for e in cold])
-    fill_ms = np.array([e[0].elapsed_time(e[1]) for e, _, _, _ in rec])
-    step_ms = np.array([e[2].elapsed_time(e[3]) for e, _, _, _ in rec])
-    with_host_ms = np.array([e[1].elapsed_time(e[3]) for e, _, _, _ in rec])
-    host_ms = np.array([h for _, _, _, h in rec])
-    tokens = np.array([t for _, t, _, _ in rec], dtype=np.float64)
-    sharers = np.array([n for _, _, n, _ in rec], dtype=np.float64)
+    fill_ms = np.array([e[0].elapsed_time(e[1]) for e, _, _, _, _ in rec])
+    step_ms = np.array([e[2].elapsed_time(e[3]) for e, _, _, _, _ in rec])
+    with_host_ms = np.array([e[1].elapsed_time(e[3]) for e, _, _, _, _ in rec])
+    host_ms = np.array([h for _, _, _, h, _ in rec])
+    wait_ms = np.array([w for _, _, _, _, w in rec])
+    tokens = np.array([t for _, t, _, _, _ in rec], dtype=np.float64)
+    sharers = np.array([n for _, _, n, _, _ in rec], dtype=np.float64)
     joins = sum(1 for j in tr.log["joins"] if warm <= j[4] < warm + steps)
     prefix = tr.prefix_tokens
     tr.drain()
     assert tr.pool.num_free == 36864, "trace leaked blocks"
     del tr.pool_d
     return dict(step_ms=step_ms, fill_ms=fill_ms, tokens=tokens, sharers=sharers, joins=joins, prefix=prefix,
-                with_host_ms=with_host_ms, host_ms=host_ms, cold_ms=cold_ms, checker=chk)
+                with_host_ms=with_host_ms, host_ms=host_ms, wait_ms=wait_ms, cold_ms=cold_ms, checker=chk)
 
 
 def measure_trace(torch, steps=300, warm=5, checkers=None):
@@ -300,6 +301,8 @@ def measure_trace(torch, steps=300, warm=5, checkers=None):
             "decode_step_cold_ms_p50": float(np.percentile(d["cold_ms"], 50)),
             "decode_step_with_host_ms_p50": float(np.percentile(d["with_host_ms"], 50)),
             "host_prep_ms_p50": float(np.percentile(d["host_ms"], 50)),
+            "host_prep_ms_p90": float(np.percentile(d["host_ms"], 90)),
+            "stage_wait_ms_p50": float(np.percentile(d["wait_ms"], 50)),
             "kv_tokens_per_s": float(tokens.sum() / (ms.sum() / 1e3)),
             "logical_tb_s": float(tokens.sum() * LAYER_TOKEN_BYTES / (ms.sum() / 1e3) / 1e12),
         }
@@ -316,7 +319,8 @@ def measure_trace(torch, steps=300, warm=5, checkers=None):
         "fill_ms_total": float(p["fill_ms"].sum()),
         "pool_drained": True,
         "host_prep_note": "one pkv_grow_rows call, staging into pinned memory and the async uploads; "
-                          "the synthetic draws are not counted",
+                          "the synthetic draws are not counted, and the wait for a free staging buffer of the "
+                          "4-deep ring (the host running ahead of the GPU) is stage_wait_ms",
     })
     rec["shared_prefix_decode"] = leg(s, {
         "sharing_rows_per_step_mean": float(sharers.mean()),

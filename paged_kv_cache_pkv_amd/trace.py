@@ -180,7 +180,9 @@ class ContinuousBatchTrace:
         (one batched table growth through the block pool, and the staging and
         asynchronous upload of tables, lengths and marks through pinned
         memory) is timed on the host and returned as snap["host_ms"]; the
-        step's synthetic inputs are drawn before it and not counted.
+        step's synthetic inputs are drawn before it and not counted, and the
+        wait for a free staging buffer (the host running ahead of the GPU) is
+        returned apart as snap["stage_wait_ms"].
         before_decode, if given, is called just before the decode part is
         queued (e.g. to scrub the caches)."""
         torch = self.torch
@@ -208,8 +210,13 @@ class ContinuousBatchTrace:
         if grown < self.max_rows:
             raise RuntimeError("block pool exhausted: the trace's pool is sized so that every row always fits")
         st = self.step_no % self.STAGES
+        wait_ms = 0.0
         if self._stage_done[st] is not None:
-            self._stage_done[st].synchronize()  # its previous upload has landed
+            # its previous upload has landed; a host that runs ahead of the
+            # GPU waits here, which is backpressure, not preparation
+            t_wait = time.perf_counter()
+            self._stage_done[st].synchronize()
+            wait_ms = (time.perf_counter() - t_wait) * 1e3
         buf = self._stage[st]
         a = buf.numpy()
         n_tab = R * self.stride
@@ -227,7 +234,7 @@ class ContinuousBatchTrace:
         ev = torch.cuda.Event()
         ev.record()
         self._stage_done[st] = ev
-        host_ms = (time.perf_counter() - t_host) * 1e3
+        host_ms = (time.perf_counter() - t_host) * 1e3 - wait_ms
         if before_decode is not None:
             before_decode()
         if events:
@@ -243,7 +250,8 @@ class ContinuousBatchTrace:
             events[3].record()
         tables = self.tables[slots].copy()
         snap = {"step": self.step_no, "reqs": [r.req for r in rows], "lens": lens.copy(),
-                "gen_index": [r.generated for r in rows], "tables": tables, "out": out, "host_ms": host_ms}
+                "gen_index": [r.generated for r in rows], "tables": tables, "out": out, "host_ms": host_ms,
+                "stage_wait_ms": wait_ms}
         self.log["steps"].append({"step": self.step_no, "reqs": snap["reqs"], "lens": lens.copy(),
                                   "new_pos": (lens - 1).copy()})
         for r in rows:
