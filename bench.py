@@ -395,6 +395,37 @@ def measure_bandwidth(torch, pkv, cache, tables, tlen, stream):
     }
 
 
+def own_slab_ceiling(torch, stream, parts, batch, NL, reps=2):
+    """Read rate of the slab probe over the (block, layer) slabs that one decode
+    launch of a given cache layout reads, every layer in turn with the
+    non-temporal policy: parts = [(tensor, slab_bytes)], each tensor
+    [blocks][NL][...] with one contiguous slab of slab_bytes per (block,
+    layer) (for example the 8-bit codes and their scales).  GB/s over whole
+    slabs."""
+    from paged_kv_cache_pkv_amd import probe
+
+    dev = parts[0][0].device
+    nblk = [-(-int(L) // 16) for L in batch.context_lens]
+    ids = np.concatenate([batch.block_tables[r, :nblk[r]] for r in range(batch.rows)]).astype(np.int64)
+    idx = torch.from_numpy(np.stack([ids * NL + l for l in range(NL)]).astype(np.int32)).to(dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def one(layer):
+        for t, sb in parts:
+            probe.slab_read(t, idx[layer], sb, sink, True, stream)
+
+    one(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps * NL):
+        one(i % NL)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * NL)
+    return len(ids) * sum(sb for _, sb in parts) / (ms / 1e3) / 1e9
+
+
 def measure_mfma_ceiling(torch, stream, iters=4000, reps=5):
     """Sustained FP16 matrix-core rate on this machine, from the probe in
     libpkv_probe.so: every SIMD kept busy with independent
@@ -640,6 +671,7 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
     ms_append = e0.elapsed_time(e1) / steps
     tokens = float(batch.context_lens.sum())
     kv_bytes = tokens * NL * 2 * kv_heads * 128 * 2
+    own = own_slab_ceiling(torch, stream, [(pool, 2 * kv_heads * 16 * 128 * 2)], batch, NL)
     del pool
     return {
         "ms_per_step_with_fused_append": ms_append,
@@ -650,6 +682,9 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
         "hbm_tb_s": kv_bytes / (ms / 1e3) / 1e12,
         "hbm_frac_of_peak": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "traffic_bytes_per_launch": fp8_gqa_traffic("gqa") if counted else None,
+        "own_layout_slab_read_gb_s": own,
+        "frac_of_own_layout_read": kv_bytes / (ms / 1e3) / 1e9 / own,
+        "own_layout_note": f"the slab probe over this pool's (block, layer) slabs of {2 * kv_heads * 4} KiB",
     }
 
 
@@ -723,6 +758,7 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
     tokens = float(batch.context_lens.sum())
     nbytes = tokens * NL * 2 * H * (128 + 4)
     layer_bytes = nbytes / NL
+    own = own_slab_ceiling(torch, stream, [(codes, 2 * H * 16 * 128), (scales, 2 * H * 16 * 4)], batch, NL)
     del codes, scales, cache
     return {
         "workload": f"average-mix decode step over an 8-bit cache: {R} rows x {NL} layers, {H} heads x 128, FP8 E4M3 "
@@ -738,6 +774,9 @@ def measure_fp8(torch, pkv, batch, stream, steps=10, warm=3):
         "decode_hbm_tb_s": layer_bytes / (launch_ms / 1e3) / 1e12,
         "decode_frac_of_peak": layer_bytes / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "decode_traffic_bytes_per_launch": fp8_gqa_traffic("fp8"),
+        "own_layout_slab_read_gb_s": own,
+        "decode_frac_of_own_layout_read": layer_bytes / (launch_ms / 1e3) / 1e9 / own,
+        "own_layout_note": "the slab probe over the codes' 128 KiB and the scales' 4 KiB (block, layer) slabs",
     }
 
 
