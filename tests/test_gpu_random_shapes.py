@@ -1,0 +1,93 @@
+"""Decode at many seeded shapes against the fp64 oracle.
+
+The other GPU tests pick their shapes by hand (edges of blocks, shares and
+ranges; many rows; long rows).  Here a seeded draw adds shapes nobody chose:
+KV heads in {1, 2, 3, 8}, 1, 2, 4 or 8 query heads per KV head, 1 to 23 rows
+of lognormal lengths up to 4,000 tokens, with and without the step's append
+fused in (FP16, grouped-query and 8-bit caches).  Each case checks every
+output element within the tolerance, and the fused cases also check the pool
+bytes against the oracle's append."""
+import numpy as np
+import pytest
+
+import oracle.fp8 as ofp8
+import oracle.paged as opaged
+import paged_kv_cache_pkv_amd as pkv
+from tests.gpu_util import dev, host_f64, say, torch_cuda
+from tests.tolerance import assert_close
+from workloads import SCALE, build_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _lengths(rng, rows):
+    return np.clip(rng.lognormal(5.5, 1.2, rows).astype(np.int64), 1, 4000).tolist()
+
+
+def _shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 3, 8]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        lens = _lengths(rng, int(rng.integers(1, 24)))
+        out.append((i, hkv, group, lens, bool(rng.integers(0, 2))))
+    return out
+
+
+CASES = _shapes(2024, 24)
+
+
+@pytest.mark.parametrize("idx,hkv,group,lens,fused", CASES,
+                         ids=[f"{c[0]}-kv{c[1]}-g{c[2]}-r{len(c[3])}-{'fused' if c[4] else 'plain'}" for c in CASES])
+def test_decode_random_shape(idx, hkv, group, lens, fused):
+    torch = torch_cuda()
+    hq = hkv * group
+    R, maxL = len(lens), max(lens)
+    b = build_batch(f"rand-{idx}", 700 + idx, lens, [1] * R, num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                    num_layers=2, num_heads=hkv, stride=-(-maxL // 16) + 1)
+    layer = 1
+    q = np.random.default_rng(900 + idx).standard_normal((R, hq, 128), dtype=np.float32).astype(np.float16)
+    q = q.view(np.uint16)
+    want_pool = opaged.append(b.pool, layer, b.k_new[layer], b.v_new[layer], b.positions, b.request_of_token,
+                              b.block_tables)
+    ref = opaged.decode(want_pool[:, layer], q, b.block_tables, b.context_lens, SCALE, group=group)
+    pool_d = dev(b.pool if fused else want_pool, torch)
+    cache = pkv.PagedCache(pool_d)
+    ws = torch.empty(max(pkv.decode_workspace_size_gqa(cache, hq, R, maxL), 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, hq, 128), dtype=torch.float16, device="cuda")
+    tables, lens_d = dev(b.block_tables, torch), dev(b.context_lens, torch)
+    say(f"random decode shape {idx}: {hkv} KV heads, G {group}, {R} rows, longest {maxL}, fused {fused}")
+    if fused:
+        pkv.decode_attention_append_gqa(cache, hq, layer, out, dev(q, torch), dev(b.k_new[layer], torch),
+                                        dev(b.v_new[layer], torch), tables, lens_d, maxL, SCALE, ws)
+    else:
+        pkv.decode_attention_gqa(cache, hq, layer, out, dev(q, torch), tables, lens_d, maxL, SCALE, ws)
+    torch.cuda.synchronize()
+    assert_close(host_f64(out), ref, f"random shape {idx}")
+    if fused:
+        assert np.array_equal(pool_d.cpu().numpy().view(np.uint16), want_pool), "fused append differs"
+
+
+FP8_CASES = [(i, int(h), _lengths(np.random.default_rng(3000 + i), int(r)))
+             for i, (h, r) in enumerate(zip(np.random.default_rng(2025).choice([1, 3, 8, 32], 10),
+                                            np.random.default_rng(2026).integers(1, 24, 10)))]
+
+
+@pytest.mark.parametrize("idx,heads,lens", FP8_CASES, ids=[f"{c[0]}-h{c[1]}-r{len(c[2])}" for c in FP8_CASES])
+def test_fp8_decode_random_shape(idx, heads, lens):
+    torch = torch_cuda()
+    R, maxL = len(lens), max(lens)
+    b = build_batch(f"rand8-{idx}", 800 + idx, lens, [1] * R, num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                    num_layers=1, num_heads=heads, stride=-(-maxL // 16) + 1)
+    pool = opaged.append(b.pool, 0, b.k_new[0], b.v_new[0], b.positions, b.request_of_token, b.block_tables)
+    codes, scales = ofp8.quantize_rows(pool)
+    ref = ofp8.decode(codes, scales, 0, b.q[0], b.block_tables, b.context_lens, SCALE)
+    cache = pkv.PagedCache8(dev(codes, torch), dev(scales, torch))
+    ws = torch.empty(max(pkv.decode_workspace_size_fp8(cache, R, maxL), 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, heads, 128), dtype=torch.float16, device="cuda")
+    say(f"random 8-bit decode shape {idx}: {heads} heads, {R} rows, longest {maxL}")
+    pkv.decode_attention_fp8(cache, 0, out, dev(b.q[0], torch), dev(b.block_tables, torch), dev(b.context_lens, torch),
+                             maxL, SCALE, ws)
+    torch.cuda.synchronize()
+    assert_close(host_f64(out), ref, f"random 8-bit shape {idx}")
