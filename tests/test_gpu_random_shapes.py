@@ -1,12 +1,13 @@
-"""Decode at many seeded shapes against the fp64 oracle.
+"""Decode and chunked prefill at many seeded shapes against the fp64 oracle.
 
 The other GPU tests pick their shapes by hand (edges of blocks, shares and
 ranges; many rows; long rows).  Here a seeded draw adds shapes nobody chose:
 KV heads in {1, 2, 3, 8}, 1, 2, 4 or 8 query heads per KV head, 1 to 23 rows
 of lognormal lengths up to 4,000 tokens, with and without the step's append
-fused in (FP16, grouped-query and 8-bit caches).  Each case checks every
-output element within the tolerance, and the fused cases also check the pool
-bytes against the oracle's append."""
+fused in (FP16, grouped-query and 8-bit caches), and prefill batches that mix
+chunks of 2 to 300 queries with decode rows.  Each case checks every output
+element within the tolerance, and the fused cases also check the pool bytes
+against the oracle's append."""
 import numpy as np
 import pytest
 
@@ -91,3 +92,47 @@ def test_fp8_decode_random_shape(idx, heads, lens):
                              maxL, SCALE, ws)
     torch.cuda.synchronize()
     assert_close(host_f64(out), ref, f"random 8-bit shape {idx}")
+
+
+def _prefill_shapes(seed, n):
+    """KV heads, group size, and rows of lognormal lengths whose query counts
+    are 1 (a decode row, about 3 in 10) or a chunk of 2 to 300 queries."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        group = int(rng.choice([1, 2, 4]))
+        lens = [max(2, L) for L in _lengths(rng, int(rng.integers(1, 13)))]
+        qc = [1 if rng.random() < 0.3 else int(rng.integers(2, min(L, 300) + 1)) for L in lens]
+        out.append((i, hkv, group, lens, qc))
+    return out
+
+
+PREFILL_CASES = _prefill_shapes(2027, 8)
+
+
+@pytest.mark.parametrize("idx,hkv,group,lens,qc", PREFILL_CASES,
+                         ids=[f"{c[0]}-kv{c[1]}-g{c[2]}-r{len(c[3])}" for c in PREFILL_CASES])
+def test_prefill_random_shape(idx, hkv, group, lens, qc):
+    torch = torch_cuda()
+    hq = hkv * group
+    R, maxL, maxq = len(lens), max(lens), max(qc)
+    b = build_batch(f"randp-{idx}", 1100 + idx, lens, qc, num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                    num_layers=1, num_heads=hkv, stride=-(-maxL // 16) + 1)
+    T = b.total_q
+    q = np.random.default_rng(1200 + idx).standard_normal((T, hq, 128), dtype=np.float32).astype(np.float16)
+    q = q.view(np.uint16)
+    pool = opaged.append(b.pool, 0, b.k_new[0], b.v_new[0], b.positions, b.request_of_token, b.block_tables)
+    ref = opaged.chunked_prefill(pool[:, 0], q, b.query_start, b.block_tables, b.context_lens, SCALE, group=group)
+    pool_d = dev(b.pool, torch)
+    cache = pkv.PagedCache(pool_d)
+    tables = dev(b.block_tables, torch)
+    pkv.append(cache, 0, dev(b.k_new[0], torch), dev(b.v_new[0], torch), dev(b.positions, torch),
+               dev(b.request_of_token, torch), tables)
+    ws = torch.empty(pkv.prefill_workspace_size_gqa(cache, hq, R, T, maxq, maxL), dtype=torch.uint8, device="cuda")
+    out = torch.full((T, hq, 128), float("nan"), dtype=torch.float16, device="cuda")
+    say(f"random prefill shape {idx}: {hkv} KV heads, G {group}, {R} rows, {T} queries, longest {maxL}")
+    pkv.chunked_prefill_attention_gqa(cache, hq, 0, out, dev(q, torch), dev(b.query_start, torch), tables,
+                                      dev(b.context_lens, torch), maxq, maxL, SCALE, ws)
+    torch.cuda.synchronize()
+    assert_close(host_f64(out), ref, f"random prefill shape {idx}")
