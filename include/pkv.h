@@ -359,6 +359,37 @@ int pkv_decode_attention_prefix(const pkv_cache* cache, int32_t layer, void* out
                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Device-side check of a step's metadata.
+ *
+ * The kernels above trust the contents of the device arrays, as the pages'
+ * gather trusts its block table (scalablesystem.dev, "PagedAttention Block
+ * Table Lookup"): a bad entry cannot make them touch memory outside their
+ * buffers, but it gives a wrong answer, and a row reading another request's
+ * blocks is on the faangrind failure list.  pkv_check_tables counts, on the
+ * device, the entries that break the contract and leaves a report there; it
+ * never synchronises the stream (read the report after the stream reaches
+ * it).  The library calls it nowhere itself: it is for debugging and for
+ * callers that want the check on every step.
+ *   block_tables, bt_stride, context_lens, num_rows, max_context_len
+ *                  as in pkv_decode_attention (scalars validated the same way)
+ *   query_start    device int32 [num_rows + 1] of a chunked-prefill step, or
+ *                  NULL to skip the query checks
+ *   total_q        the prefill step's query count (used with query_start)
+ *   report         device int32 [4], overwritten completely by the call:
+ *     [0] rows whose length is outside [1, max_context_len]
+ *     [1] table entries outside [0, num_blocks) among those the kernels read
+ *         (the first ceil(min(L, max_context_len) / 16) of each row)
+ *     [2] rows whose query range breaks the prefill contract: query_start[r]
+ *         < 0, query_start[r + 1] > total_q, n_r < 1 or n_r > L (0 without
+ *         query_start)
+ *     [3] the smallest row with any violation, or -1
+ * One workgroup; no global atomics, nothing to clear beforehand, so it can be
+ * captured and replayed.  num_rows >= 1. */
+int pkv_check_tables(const pkv_cache* cache, const int32_t* block_tables, int32_t bt_stride,
+                     const int32_t* context_lens, int32_t num_rows, int32_t max_context_len,
+                     const int32_t* query_start, int32_t total_q, int32_t* report, void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole-block copies.
  *
  * A block with all its layers is one contiguous region of the pool of

@@ -292,6 +292,23 @@ def decode_attention_prefix(cache: PagedCache, layer: int, out, q, block_tables,
                                              _stream_ptr(stream)))
 
 
+def check_tables(cache: PagedCache, block_tables, context_lens, max_context_len: int, report, query_start=None,
+                 total_q: int = 0, stream=None):
+    """Count on the device the table entries, lengths and (with `query_start`)
+    query ranges that break the calls' contract; `report` (device int32 [4])
+    receives [bad lengths, bad table entries, bad query ranges, first bad row
+    or -1].  Asynchronous: read `report` after the stream reaches it."""
+    R, stride = (int(x) for x in block_tables.shape)
+    _need(context_lens, R, "context_lens")
+    _need(report, 4, "report")
+    if query_start is not None:
+        _need(query_start, R + 1, "query_start")
+    _check(lib().pkv_check_tables(ctypes.byref(cache.desc), _dptr(block_tables, "block_tables", 4), stride,
+                                  _dptr(context_lens, "context_lens", 4), R, int(max_context_len),
+                                  _dptr(query_start, "query_start", 4),
+                                  int(total_q), _dptr(report, "report", 4), _stream_ptr(stream)))
+
+
 def prefill_workspace_size(cache: PagedCache, num_rows: int, total_q: int, max_q_per_row: int,
                            max_context_len: int) -> int:
     return int(lib().pkv_prefill_workspace_size(ctypes.byref(cache.desc), int(num_rows), int(total_q),

@@ -64,6 +64,7 @@ SIGNATURES = {
     "pkv_decode_workspace_size_prefix": (c_size, [PkvCacheDesc_p, c_i32, c_i32, c_i32]),
     "pkv_decode_attention_prefix": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
                                                    ctypes.c_float, c_vp, c_i32, c_vp, c_size, c_vp]),
+    "pkv_check_tables": (ctypes.c_int, [PkvCacheDesc_p, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_decode_workspace_size_gqa": (c_size, [PkvCacheDesc_p, c_i32, c_i32, c_i32]),
     "pkv_decode_attention_gqa": (ctypes.c_int, [PkvCacheDesc_p, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32,
                                                 c_i32, ctypes.c_float, c_vp, c_size, c_vp]),

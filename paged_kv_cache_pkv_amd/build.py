@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")  # bandwidth probes: a measurement aid, not the product ABI
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["errors.cpp", "pool.cpp", "append.hip", "decode.hip", "prefill.hip", "blocks.hip", "fp8.hip", "prefix.hip"]
+SOURCES = ["errors.cpp", "pool.cpp", "append.hip", "decode.hip", "prefill.hip", "blocks.hip", "fp8.hip", "prefix.hip", "check.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -226,6 +226,24 @@ def test_validation_prefix_decode():
     assert call(125, stride=256, maxL=4096, ws=None) == -6
 
 
+def test_validation_check_tables():
+    L = pkv.lib()
+    d = _desc()
+
+    def call(R=4, stride=16, maxL=256, bt=FAKE, cl=FAKE, qs=None, total_q=0, rep=FAKE, desc=d):
+        return L.pkv_check_tables(ctypes.byref(desc), bt, stride, cl, R, maxL, qs, total_q, rep, None)
+    assert call(R=0) == -1
+    assert call(stride=0) == -1
+    assert call(maxL=0) == -1
+    assert call(maxL=16 * 16 + 1) == -1
+    assert call(bt=None) == -1
+    assert call(cl=None) == -1
+    assert call(rep=None) == -1
+    assert call(qs=FAKE, total_q=0) == -1  # query checks need the step's query count
+    assert call(desc=_desc(head_dim=64)) == -2
+    assert L.pkv_last_error()
+
+
 def test_validation_block_copies():
     L = pkv.lib()
     d = _desc(num_layers=3, num_heads=5)
