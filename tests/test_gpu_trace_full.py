@@ -31,12 +31,20 @@ def test_trace_full_size_parity(shared_decode):
 
     tr = ContinuousBatchTrace(torch, seed=3, num_blocks=NB, max_rows=64, prefix_tokens=2000,
                               prompt_range=(50, 8000), answer_range=(1, 1000), shared_decode=shared_decode)
+    import paged_kv_cache_pkv_amd as pkv
+
     chk = TraceChecker(tr)
     npre = len(tr.prefix_ids)
     assert npre == 125
     max_sharers = 0
+    # every step's uploaded tables and lengths, checked on the device after the step's launches
+    reports = torch.full((STEPS, 4), -9, dtype=torch.int32, device=tr.dev)
     for s in range(STEPS):
         snap = tr.step()
+        R = len(snap["reqs"])
+        n_tab = R * tr.stride
+        pkv.check_tables(tr.cache, tr.meta_d[:n_tab].view(R, tr.stride), tr.meta_d[n_tab:n_tab + R], tr.max_ctx,
+                         reports[s])
         chk.record(snap)
         sharers = sum(1 for r in tr.rows if r.shared)
         max_sharers = max(max_sharers, sharers)
@@ -48,6 +56,8 @@ def test_trace_full_size_parity(shared_decode):
             chk.keep(snap)
             say(f"trace step {s} ({'shared-prefix' if shared_decode else 'appending'} decode): {len(snap['reqs'])} "
                 f"rows, {sharers} sharing the prefix, context {int(snap['lens'].min())}..{int(snap['lens'].max())}")
+    rep = reports.cpu().numpy()
+    assert (rep[:, :3] == 0).all() and (rep[:, 3] == -1).all(), rep[(rep[:, :3] != 0).any(axis=1)][:4]
     assert max_sharers > 32, "the prefix must be shared by more rows than one tile holds"
     # answers are U{1..1000} tokens, so over 300 steps some 15-20 rows finish and are refilled
     joins = len(tr.log["joins"])
