@@ -71,8 +71,9 @@ def counted_record(path, sources):
 
 
 def fp8_gqa_traffic(kind):
-    """HBM bytes per 8-bit ("fp8") or grouped-query ("gqa") decode launch from
-    the committed counter summary, or None when its sources have changed."""
+    """HBM bytes per 8-bit ("fp8") or grouped-query ("gqa": groups of 4, "gqa8":
+    groups of 8) decode call from the committed counter summary, or None when
+    its sources have changed."""
     try:
         with open(FP8_GQA_COUNTERS) as f:
             rec = json.load(f)
@@ -607,13 +608,14 @@ def measure_long_context(torch, pkv, cache, stream, steps=5, warm=2):
     }
 
 
-def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, warm=3, payload=None, counted=True):
+def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, warm=3, payload=None, counted="gqa"):
     """Grouped-query decode: the average mix's tables and lengths over a
     32-layer pool of kv_heads KV heads, q_heads query heads (8 and 32: groups
     of 4; 4 and 32: groups of 8); per layer one decode launch.  Bytes = K and
     V of the KV heads per token.  With `payload` (a list), layer 0's first
     output and the blocks it read are kept for the oracle leg.  `counted`:
-    the committed counter summary covers this shape (groups of 4)."""
+    this shape's key in the committed counter summary ("gqa" for groups of 4,
+    "gqa8" for groups of 8), or None."""
     from workloads import SCALE, fill_normal_fp16_device
 
     NB, NL = 7152, 32
@@ -681,7 +683,7 @@ def measure_gqa(torch, pkv, batch, stream, kv_heads=8, q_heads=32, steps=10, war
         "kv_tokens_per_s": tokens / (ms / 1e3),
         "hbm_tb_s": kv_bytes / (ms / 1e3) / 1e12,
         "hbm_frac_of_peak": kv_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-        "traffic_bytes_per_launch": fp8_gqa_traffic("gqa") if counted else None,
+        "traffic_bytes_per_launch": fp8_gqa_traffic(counted) if counted else None,
         "own_layout_slab_read_gb_s": own,
         "frac_of_own_layout_read": kv_bytes / (ms / 1e3) / 1e9 / own,
         "own_layout_note": f"the slab probe over this pool's (block, layer) slabs of {2 * kv_heads * 4} KiB",
@@ -1078,7 +1080,7 @@ def main():
         del pool_d, cache
         torch.cuda.empty_cache()
         gqa = measure_gqa(torch, pkv, batch, stream, payload=gqa_payload)
-        gqa8 = measure_gqa(torch, pkv, batch, stream, kv_heads=4, q_heads=32, payload=gqa8_payload, counted=False)
+        gqa8 = measure_gqa(torch, pkv, batch, stream, kv_heads=4, q_heads=32, payload=gqa8_payload, counted="gqa8")
         fp8 = measure_fp8(torch, pkv, batch, stream)
         tiny = measure_tiny(torch, pkv, dev, stream)
     else:
