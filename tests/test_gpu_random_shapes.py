@@ -4,10 +4,12 @@ The other GPU tests pick their shapes by hand (edges of blocks, shares and
 ranges; many rows; long rows).  Here a seeded draw adds shapes nobody chose:
 KV heads in {1, 2, 3, 8}, 1, 2, 4 or 8 query heads per KV head, 1 to 23 rows
 of lognormal lengths up to 4,000 tokens, with and without the step's append
-fused in (FP16, grouped-query and 8-bit caches), and prefill batches that mix
-chunks of 2 to 300 queries with decode rows.  Each case checks every output
-element within the tolerance, and the fused cases also check the pool bytes
-against the oracle's append."""
+fused in (FP16, grouped-query and 8-bit caches), prefill batches that mix
+chunks of 2 to 300 queries with decode rows, and shared-prefix decode batches
+(prefixes of 1 to 47 blocks, sharing, unmarked and marked-but-short rows).
+Each case checks every output element within the tolerance; the fused cases
+also check the pool bytes against the oracle's append, and the prefix cases
+that rows off the shared path give the plain decode's bits."""
 import numpy as np
 import pytest
 
@@ -136,3 +138,65 @@ def test_prefill_random_shape(idx, hkv, group, lens, qc):
                                       dev(b.context_lens, torch), maxq, maxL, SCALE, ws)
     torch.cuda.synchronize()
     assert_close(host_f64(out), ref, f"random prefill shape {idx}")
+
+
+def _prefix_shapes(seed, n):
+    """(idx, P, heads, lens, shared rows, lone rows): row 0 holds a prefix of P
+    blocks that the shared rows reference; lone rows are marked but end inside
+    the prefix's length (private tables), the rest are unmarked."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        P = int(rng.integers(1, 48))
+        heads = int(rng.choice([8, 32]))
+        rows = int(rng.integers(2, 48))
+        lens, shared, lone = [], [], []
+        for r in range(rows):
+            kind = 0 if r == 0 else int(rng.choice(3, p=[0.6, 0.25, 0.15]))
+            if kind == 0:
+                lens.append(16 * P + 1 + int(min(rng.lognormal(5.0, 1.2), 3000)))
+                if r:
+                    shared.append(r)
+            elif kind == 1:
+                lens.append(int(np.clip(rng.lognormal(6.0, 1.2), 1, 5000)))
+            else:
+                lens.append(int(rng.integers(1, 16 * P + 1)))
+                lone.append(r)
+        out.append((i, P, heads, lens, shared, lone))
+    return out
+
+
+PREFIX_CASES = _prefix_shapes(2031, 8)
+
+
+@pytest.mark.parametrize("idx,P,heads,lens,shared,lone", PREFIX_CASES,
+                         ids=[f"{c[0]}-P{c[1]}-h{c[2]}-r{len(c[3])}-s{len(c[4])}" for c in PREFIX_CASES])
+def test_prefix_decode_random_shape(idx, P, heads, lens, shared, lone):
+    torch = torch_cuda()
+    R = len(lens)
+    nblk = [-(-L // 16) for L in lens]
+    say(f"random prefix decode {idx}: P={P}, {heads} heads, {R} rows ({len(shared)} sharing, {len(lone)} lone), "
+        f"lengths {min(lens)}..{max(lens)}")
+    b = build_batch(f"rand-prefix-{idx}", 1300 + idx, lens, [1] * R, num_blocks=sum(nblk) - len(shared) * P + 8,
+                    num_heads=heads, stride=max(nblk), shared_prefix_blocks=P, shared_rows=shared)
+    pool = opaged.append(b.pool, 0, b.k_new[0], b.v_new[0], b.positions, b.request_of_token, b.block_tables)
+    ref = opaged.decode(pool[:, 0], b.q[0], b.block_tables, b.context_lens, SCALE)
+    marks = np.zeros(R, dtype=np.int32)
+    marks[[0, *shared, *lone]] = 1
+    pool_d = dev(pool, torch)
+    cache = pkv.PagedCache(pool_d)
+    maxL = max(lens)
+    tables, lens_d, q = dev(b.block_tables, torch), dev(b.context_lens, torch), dev(b.q[0], torch)
+    ws = torch.empty(max(pkv.decode_workspace_size_prefix(cache, R, maxL, P), 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, heads, 128), dtype=torch.float16, device="cuda")
+    pkv.decode_attention_prefix(cache, 0, out, q, tables, lens_d, maxL, SCALE, dev(marks, torch), P, ws)
+    ws2 = torch.empty(max(pkv.decode_workspace_size(cache, R, maxL), 256), dtype=torch.uint8, device="cuda")
+    plain = torch.empty_like(out)
+    pkv.decode_attention(cache, 0, plain, q, tables, lens_d, maxL, SCALE, ws2)
+    torch.cuda.synchronize()
+    assert_close(host_f64(out), ref, f"random prefix decode {idx}")
+    # rows that do not take the shared path (unmarked, or ending inside the prefix) give the plain decode's bits
+    got, want = out.cpu().numpy().view(np.uint16), plain.cpu().numpy().view(np.uint16)
+    for r in range(R):
+        if not (marks[r] and lens[r] > 16 * P):
+            assert np.array_equal(got[r], want[r]), (idx, r)
