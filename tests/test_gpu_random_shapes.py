@@ -6,7 +6,9 @@ KV heads in {1, 2, 3, 8}, 1, 2, 4 or 8 query heads per KV head, 1 to 23 rows
 of lognormal lengths up to 4,000 tokens, with and without the step's append
 fused in (FP16, grouped-query and 8-bit caches), prefill batches that mix
 chunks of 2 to 300 queries with decode rows, and shared-prefix decode batches
-(prefixes of 1 to 47 blocks, sharing, unmarked and marked-but-short rows).
+(prefixes of 1 to 47 blocks, sharing, unmarked and marked-but-short rows),
+and FP16 and 8-bit appends of flat token lists of up to 300 tokens per row
+(bit-exact over the whole pool).
 Each case checks every output element within the tolerance; the fused cases
 also check the pool bytes against the oracle's append, and the prefix cases
 that rows off the shared path give the plain decode's bits."""
@@ -200,3 +202,49 @@ def test_prefix_decode_random_shape(idx, P, heads, lens, shared, lone):
     for r in range(R):
         if not (marks[r] and lens[r] > 16 * P):
             assert np.array_equal(got[r], want[r]), (idx, r)
+
+
+def _append_shapes(seed, n):
+    """(idx, heads, layers, layer, lens, new-token counts): rows gaining 1 to
+    300 tokens at once, over pools of 1 to 3 layers."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        heads = int(rng.choice([1, 3, 8, 32]))
+        layers = int(rng.integers(1, 4))
+        rows = int(rng.integers(1, 20))
+        lens = _lengths(rng, rows)
+        counts = [int(min(L, rng.choice([1, 1, int(rng.integers(1, 301))]))) for L in lens]
+        out.append((i, heads, layers, int(rng.integers(0, layers)), lens, counts))
+    return out
+
+
+APPEND_CASES = _append_shapes(2033, 10)
+
+
+@pytest.mark.parametrize("idx,heads,layers,layer,lens,counts", APPEND_CASES,
+                         ids=[f"{c[0]}-h{c[1]}-l{c[2]}-r{len(c[4])}-t{sum(c[5])}" for c in APPEND_CASES])
+def test_append_random_shape(idx, heads, layers, layer, lens, counts):
+    """FP16 and 8-bit appends of a seeded flat token list, bit-exact over the
+    whole pool (codes and scales for the 8-bit cache)."""
+    torch = torch_cuda()
+    R = len(lens)
+    b = build_batch(f"rand-append-{idx}", 1400 + idx, lens, counts, num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                    num_layers=layers, num_heads=heads, stride=-(-max(lens) // 16) + 1)
+    say(f"random append {idx}: {heads} heads, {layers} layers (layer {layer}), {R} rows, {sum(counts)} tokens")
+    want = opaged.append(b.pool, layer, b.k_new[layer], b.v_new[layer], b.positions, b.request_of_token,
+                         b.block_tables)
+    pos, rows, tables = dev(b.positions, torch), dev(b.request_of_token, torch), dev(b.block_tables, torch)
+    k, v = dev(b.k_new[layer], torch), dev(b.v_new[layer], torch)
+    pool_d = dev(b.pool, torch)
+    pkv.append(pkv.PagedCache(pool_d), layer, k, v, pos, rows, tables)
+    # the 8-bit cache: every row of the pool quantized, then the same tokens appended
+    codes, scales = ofp8.quantize_rows(b.pool)
+    want_c, want_s = ofp8.append(codes, scales, layer, b.k_new[layer], b.v_new[layer], b.positions,
+                                 b.request_of_token, b.block_tables)
+    codes_d, scales_d = dev(codes, torch), dev(scales, torch)
+    pkv.append_fp8(pkv.PagedCache8(codes_d, scales_d), layer, k, v, pos, rows, tables)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_d.cpu().numpy().view(np.uint16), want)
+    assert np.array_equal(codes_d.cpu().numpy(), want_c)
+    assert np.array_equal(scales_d.cpu().numpy().view(np.uint32), np.asarray(want_s).view(np.uint32))
