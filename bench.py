@@ -1079,15 +1079,17 @@ def main():
         probe = measure_bandwidth(torch, pkv, cache, tables, tlen, stream)
         blocks = measure_block_copies(torch, pkv, cache, bp.free_list(), stream)
         long_ctx = measure_long_context(torch, pkv, cache, stream)
+        # The 60 GB pool goes back to torch's cache, not to the driver: the
+        # later legs' pools are carved from it.  A 60 GB free to the driver
+        # slowed every read on the device by about 8% for tens of seconds
+        # afterwards (most plausibly the driver clearing the freed memory).
         del pool_d, cache
-        torch.cuda.empty_cache()
         gqa = measure_gqa(torch, pkv, batch, stream, payload=gqa_payload)
         gqa8 = measure_gqa(torch, pkv, batch, stream, kv_heads=4, q_heads=32, payload=gqa8_payload, counted="gqa8")
         fp8 = measure_fp8(torch, pkv, batch, stream)
         tiny = measure_tiny(torch, pkv, dev, stream)
     else:
         del pool_d, cache
-        torch.cuda.empty_cache()
 
     prefill = None
     if not args.no_prefill:
