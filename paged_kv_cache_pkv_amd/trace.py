@@ -77,7 +77,8 @@ class ContinuousBatchTrace:
         self.answer_range = answer_range
         self.dev = torch.device(device)
         max_ctx = prompt_range[1] + answer_range[1]
-        self.stride = stride or -(-max_ctx // BLOCK_SIZE)
+        # the shared-prefix call needs the prefix's blocks to fit the table
+        self.stride = stride or max(-(-max_ctx // BLOCK_SIZE), self.prefix_tokens // BLOCK_SIZE)
         self.scale = scale if scale is not None else 1.0 / np.sqrt(128.0)
         self.pool_d = torch.empty((num_blocks, 1, 2, heads, BLOCK_SIZE, 128), dtype=torch.float16, device=self.dev)
         gen = torch.Generator(device=self.dev)
