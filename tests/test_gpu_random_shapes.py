@@ -7,14 +7,16 @@ of lognormal lengths up to 4,000 tokens, with and without the step's append
 fused in (FP16, grouped-query and 8-bit caches), prefill batches that mix
 chunks of 2 to 300 queries with decode rows, and shared-prefix decode batches
 (prefixes of 1 to 47 blocks, sharing, unmarked and marked-but-short rows),
-and FP16 and 8-bit appends of flat token lists of up to 300 tokens per row
-(bit-exact over the whole pool).
+FP16 and 8-bit appends of flat token lists of up to 300 tokens per row
+(bit-exact over the whole pool), and block copies and swaps of seeded id
+lists (bit-exact over the pool and the host image).
 Each case checks every output element within the tolerance; the fused cases
 also check the pool bytes against the oracle's append, and the prefix cases
 that rows off the shared path give the plain decode's bits."""
 import numpy as np
 import pytest
 
+import oracle.blocks as oblocks
 import oracle.fp8 as ofp8
 import oracle.paged as opaged
 import paged_kv_cache_pkv_amd as pkv
@@ -248,3 +250,44 @@ def test_append_random_shape(idx, heads, layers, layer, lens, counts):
     assert np.array_equal(pool_d.cpu().numpy().view(np.uint16), want)
     assert np.array_equal(codes_d.cpu().numpy(), want_c)
     assert np.array_equal(scales_d.cpu().numpy().view(np.uint32), np.asarray(want_s).view(np.uint32))
+
+
+COPY_CASES = [(i, int(layers), int(heads)) for i, (layers, heads) in
+              enumerate(zip(np.random.default_rng(2035).choice([1, 2, 3, 8], 6),
+                            np.random.default_rng(2036).choice([1, 5, 8, 32], 6)))]
+
+
+@pytest.mark.parametrize("idx,layers,heads", COPY_CASES, ids=[f"{c[0]}-l{c[1]}-h{c[2]}" for c in COPY_CASES])
+def test_block_copies_random_shape(idx, layers, heads):
+    """Copy-on-write of a seeded set of pairs (distinct destinations, none a
+    source; some ids outside the pool, which are skipped), then a swap out and
+    back in of seeded id lists: the whole pool and host image bit-exact."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(1500 + idx)
+    nb = int(rng.integers(8, 80))
+    pool = rng.standard_normal((nb, layers, 2, heads, 16, 128), dtype=np.float32).astype(np.float16).view(np.uint16)
+    perm = rng.permutation(nb)
+    n = int(rng.integers(0, nb // 2 + 1))
+    src, dst = perm[:n].astype(np.int32), perm[n:2 * n].astype(np.int32)
+    if n:
+        src[rng.integers(n)] = nb + int(rng.integers(0, 5))   # skipped pair
+        dst[rng.integers(n)] = -1 - int(rng.integers(0, 5))   # skipped pair
+    say(f"random block copies {idx}: {nb} blocks of {layers} layers x {heads} heads, {n} pairs")
+    pool_d = dev(pool, torch)
+    cache = pkv.PagedCache(pool_d)
+    pkv.copy_blocks(cache, dev(src, torch), dev(dst, torch))
+    torch.cuda.synchronize()
+    want = oblocks.copy_blocks(pool, src, dst)
+    assert np.array_equal(pool_d.cpu().numpy().view(np.uint16), want)
+    # swap out a seeded id list (runs of consecutive ids and single ids), then in to other ids
+    ids = np.sort(rng.choice(nb, size=int(rng.integers(1, nb // 2 + 1)), replace=False)).tolist()
+    back = rng.permutation(nb)[:len(ids)].tolist()
+    bb = pkv.block_bytes(cache)
+    host = torch.empty(len(ids) * bb, dtype=torch.uint8, pin_memory=True)
+    pkv.swap_out(cache, ids, host)
+    torch.cuda.synchronize()
+    image = host.numpy().view(np.uint16).reshape(len(ids), layers, 2, heads, 16, 128)
+    assert np.array_equal(image, oblocks.swap_out(want, ids))
+    pkv.swap_in(cache, host, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_d.cpu().numpy().view(np.uint16), oblocks.swap_in(want, image, back))
