@@ -291,3 +291,35 @@ def test_block_copies_random_shape(idx, layers, heads):
     pkv.swap_in(cache, host, back)
     torch.cuda.synchronize()
     assert np.array_equal(pool_d.cpu().numpy().view(np.uint16), oblocks.swap_in(want, image, back))
+
+
+FP8_FUSED_CASES = [(i, int(h), _lengths(np.random.default_rng(3100 + i), int(r)))
+                   for i, (h, r) in enumerate(zip(np.random.default_rng(2037).choice([1, 3, 8, 32], 6),
+                                                  np.random.default_rng(2038).integers(1, 24, 6)))]
+
+
+@pytest.mark.parametrize("idx,heads,lens", FP8_FUSED_CASES,
+                         ids=[f"{c[0]}-h{c[1]}-r{len(c[2])}" for c in FP8_FUSED_CASES])
+def test_fp8_fused_append_decode_random_shape(idx, heads, lens):
+    """The 8-bit decode with the step's append fused in: codes and scales
+    bit-exact against the oracle's 8-bit append, the output within the
+    tolerance of the oracle over the appended, dequantized cache."""
+    torch = torch_cuda()
+    R, maxL = len(lens), max(lens)
+    b = build_batch(f"rand8f-{idx}", 1600 + idx, lens, [1] * R, num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                    num_layers=1, num_heads=heads, stride=-(-maxL // 16) + 1)
+    codes, scales = ofp8.quantize_rows(b.pool)
+    want_c, want_s = ofp8.append(codes, scales, 0, b.k_new[0], b.v_new[0], b.positions, b.request_of_token,
+                                 b.block_tables)
+    ref = ofp8.decode(want_c, want_s, 0, b.q[0], b.block_tables, b.context_lens, SCALE)
+    codes_d, scales_d = dev(codes, torch), dev(scales, torch)
+    cache = pkv.PagedCache8(codes_d, scales_d)
+    ws = torch.empty(max(pkv.decode_workspace_size_fp8(cache, R, maxL), 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, heads, 128), dtype=torch.float16, device="cuda")
+    say(f"random fused 8-bit decode {idx}: {heads} heads, {R} rows, longest {maxL}")
+    pkv.decode_attention_append_fp8(cache, 0, out, dev(b.q[0], torch), dev(b.k_new[0], torch), dev(b.v_new[0], torch),
+                                    dev(b.block_tables, torch), dev(b.context_lens, torch), maxL, SCALE, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_d.cpu().numpy(), want_c)
+    assert np.array_equal(scales_d.cpu().numpy().view(np.uint32), np.asarray(want_s).view(np.uint32))
+    assert_close(host_f64(out), ref, f"random fused 8-bit shape {idx}")
